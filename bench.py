@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Verified tree nodes/s through one gated-delta-rule layer on one MI355X.
+
+One step = tree_verify + tree_commit over one batch of the 64-node workload
+(B=32 sequences, H=32 heads, d_k=d_v=128, bf16 q/k/v, fp32 state, a random
+64-node draft tree per sequence, accepted node uniform over nodes).  Inputs
+are seeded synthetic data, resident in HBM before timing starts.
+
+Timing: W warm-up steps, then K timed steps.  Inside each step the L2 and the
+256 MB Infinity Cache are flushed (a 1 GiB write) before each kernel, so each
+kernel streams its operands from HBM as it would between the rest of a model
+forward; HIP events on the launch stream time each kernel, flushes excluded.
+ms_per_step = mean verify + mean commit kernel time; value = B*N / that.
+The wall time of the whole timed region (flushes included) is reported too.
+
+Prints ONE JSON line.  Options: --steps K --warmup W --gpus 1 (only 1 is
+supported: the path runs on one GPU) --workload {3,4,5} --vblock {0,32,64,128}
+--no-cpu-baseline --no-flush.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from tree_speculative_verification_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verified tree nodes/s per GDN layer (1 GPU) + % of HBM roofline"
+KERNEL_SOURCES = {
+    "verify": ["tree_speculative_verification_amd/csrc/tv_verify_mfma.hip",
+               "tree_speculative_verification_amd/csrc/tv_device.h"],
+    "commit": ["tree_speculative_verification_amd/csrc/tv_commit.hip",
+               "tree_speculative_verification_amd/csrc/tv_device.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def path_lengths(parents, accepted):
+    L = np.zeros(len(accepted), dtype=np.int64)
+    for b, a in enumerate(accepted):
+        n, c = int(a), 0
+        while n >= 0:
+            c += 1
+            n = int(parents[b, n])
+        L[b] = c
+    return L
+
+
+def algorithmic_bytes(bt):
+    """Bytes each kernel must move at least once (inputs read, outputs written)."""
+    B, N, H, dk, dv = bt.B, bt.N, bt.H, bt.dk, bt.dv
+    s = 2 if bt.dtype == synth.BF16 else 4
+    gates = 8 * N if bt.mode == synth.GDN else 4 * N
+    verify_bh = 4 * dk * dv + N * (2 * dk + dv) * s + gates + N * dv * s + 4 * N * dv
+    verify = B * H * verify_bh + B * (4 * N + 4)
+    L = path_lengths(bt.parents, bt.accepted)
+    commit = int(np.sum(H * (8 * dk * dv + L * (dk * s + 4 * dv + 4)))) + B * (4 * N + 4 + 4 + 4 * N)
+    return int(verify), int(commit), L
+
+
+def sources_sha(kind):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(f"{kind}_w{workload}")
+    if not r or r.get("source_sha") != sources_sha(kind):
+        return None
+    return r.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------ CPU baseline
+
+_CPU_BATCH = None
+
+
+def _oracle_seq(b):
+    import oracle
+    bt = _CPU_BATCH
+    sub = bt.select([b], np.arange(bt.H))
+    oracle.verify(sub.mode, sub.parents, sub.q, sub.k, sub.v, sub.alpha, sub.beta, sub.S_root)
+    oracle.commit(sub.mode, sub.parents, sub.accepted, sub.k, sub.v, sub.alpha, sub.beta, sub.S_root)
+    return b
+
+
+def cpu_baseline(bt, max_seqs):
+    """The fp64 oracle (as it stands) over whole sequences, one process per core.
+
+    Runs before the GPU is touched (the pool forks).  Returns nodes/s scaled to
+    the metric: sequences done * N / wall seconds.
+    """
+    global _CPU_BATCH
+    import multiprocessing as mp
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    _CPU_BATCH = bt
+    seqs = list(range(min(bt.B, max_seqs)))
+    cores = min(len(os.sched_getaffinity(0)), 16, len(seqs))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        list(pool.imap_unordered(_oracle_seq, seqs))
+    wall = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": len(seqs) * bt.N / wall, "unit": "nodes/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(seqs)} of {bt.B} sequences x all {bt.H} heads of the same workload "
+                      f"(fp64 token-by-token path walk, verify + commit), wall {wall:.2f} s on "
+                      f"{cores} worker processes, 1 BLAS thread each; {cpu_model}"}
+
+
+# --------------------------------------------------------------- GPU timing
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5])
+    ap.add_argument("--vblock", type=int, default=0, choices=[0, 32, 64, 128])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--no-flush", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py: --gpus {a.gpus} is not supported; this path runs on one GPU "
+              "(every (sequence, head) is independent, so more GPUs only split the batch).",
+              file=sys.stderr)
+        return 2
+    if int(os.environ.get("RANK", "0")) != 0:
+        return 0
+
+    bt = synth.make_inputs(a.workload)
+    cpu = None if a.no_cpu_baseline else cpu_baseline(bt, a.cpu_seqs)
+
+    import torch
+    from tree_speculative_verification_amd import binding as tvb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = synth.to_torch(bt, dev)
+    B, N, H, dk, dv = bt.B, bt.N, bt.H, bt.dk, bt.dv
+    o = torch.empty((B, N, H, dv), dtype=t["q"].dtype, device=dev)
+    U = torch.empty((B, H, N, dv), dtype=torch.float32, device=dev)
+    st_v = torch.empty((B,), dtype=torch.int32, device=dev)
+    S_out = torch.empty_like(t["S_root"])
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    st_c = torch.empty((B,), dtype=torch.int32, device=dev)
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    stream = torch.cuda.current_stream()
+
+    def flush():
+        if not a.no_flush:
+            flush_buf.fill_(1.0)
+
+    def verify():
+        tvb.verify(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["parents"], t["S_root"],
+                   mode=bt.mode, vblock=a.vblock, o=o, U=U, status=st_v, stream=stream)
+
+    def commit():
+        tvb.commit(t["k"], t["alpha"], U, t["parents"], t["accepted"], t["S_root"], S_out=S_out,
+                   path_out=path, status=st_c, stream=stream)
+
+    for _ in range(a.warmup):
+        flush()
+        verify()
+        flush()
+        commit()
+    torch.cuda.synchronize()
+    if st_v.any().item() or st_c.any().item():
+        raise RuntimeError("device status reported bad input rows")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(a.steps):
+        flush()
+        ev[i][0].record(stream)
+        verify()
+        ev[i][1].record(stream)
+        flush()
+        ev[i][2].record(stream)
+        commit()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    tv = np.array([e[0].elapsed_time(e[1]) for e in ev])   # ms
+    tc = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    # back-to-back without flushes (caches may hold operands): secondary figure
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        verify()
+        commit()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / a.steps
+
+    ms_step = float(tv.mean() + tc.mean())
+    value = B * N / (ms_step * 1e-3)
+    vbytes, cbytes, L = algorithmic_bytes(bt)
+    kern = {}
+    for name, ms, nbytes in (("verify", tv.mean(), vbytes), ("commit", tc.mean(), cbytes)):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        kern[name] = {"mean_us": round(ms * 1e3, 2), "median_us": round(float(np.median(tv if name == "verify" else tc)) * 1e3, 2),
+                      "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
+                      "frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "traffic": measured_traffic(name, a.workload)}
+    dom = "verify" if tv.mean() >= tc.mean() else "commit"
+    combined_gbs = (vbytes + cbytes) / (ms_step * 1e-3) / 1e9
+    snap = B * H * N * dk * dv * 4
+    u_only = B * H * N * dv * 4
+    u_k_g = B * H * N * (4 * dv + (2 if bt.dtype == synth.BF16 else 4) * dk + 4)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": synth.CONFIG_NAMES[a.workload], "B": B, "H": H, "N": N,
+                   "d_k": dk, "d_v": dv, "qkv": "bf16", "state": "fp32", "layer": "gated delta rule",
+                   "mean_path_len": round(float(L.mean()), 3), "vblock": a.vblock or "auto",
+                   "timing": "HIP events per kernel on the launch stream, L2+MALL flushed "
+                             "before each kernel (flush excluded)" if not a.no_flush else
+                             "HIP events per kernel, no flush"},
+        "roofline": {"bound": "hbm", "achieved": kern[dom]["achieved_GBs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": kern[dom]["frac"], "traffic": kern[dom]["traffic"],
+                     "kernel": dom},
+        "kernels": kern,
+        "verify_plus_commit": {"achieved_GBs": round(combined_gbs, 1),
+                               "frac": round(combined_gbs / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes": vbytes + cbytes},
+        "wall_ms_per_step_incl_flush": round(wall * 1e3 / a.steps, 4),
+        "warm_ms_per_step_no_flush": round(warm_ms, 5),
+        "transient_state_bytes": {"per_node_snapshots": snap, "U_only": u_only,
+                                  "U_plus_K_and_gates": u_k_g,
+                                  "ratio_snapshots_to_U": round(snap / u_only, 2),
+                                  "ratio_snapshots_to_U_K_gates": round(snap / u_k_g, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

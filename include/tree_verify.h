@@ -1,0 +1,160 @@
+/*
+ * tree_verify.h -- C ABI of libtreeverify.so: parallel verification of every
+ * node of a speculative draft tree through one recurrent linear-attention
+ * layer, and reconstruction of only the accepted node's state.  gfx950
+ * (MI355X) only.
+ *
+ * Method (the pages this follows):
+ *   - Twig (arXiv 2608.01651 v2) abstract / Bole (v1) abstract: a
+ *     tree-structured factorization (closed form) of the linear-attention
+ *     recurrence lets one kernel verify all draft nodes in parallel; speculative
+ *     state updates are kept as token-level factors and only the accepted
+ *     state is rebuilt.
+ *   - TreeWY (arXiv 2608.20961) abstract: for the gated delta rule, a
+ *     tree-structured WY transform gives every draft node's output from a
+ *     single triangular solve and stores a small pseudo-value matrix instead
+ *     of per-node states; the accepted state is reconstructed on commit.
+ *   - Bole paper-daily auto-summary, core-formula section and worked example:
+ *     scalar-decay linear attention S_t = lambda S_{t-1} + k_t v_t^T, its tree
+ *     closed form, and the accepted-state rebuild from S_root.
+ *
+ * Layer (per sequence b and head h; S is d_k x d_v, d_v fastest):
+ *   gated delta rule (mode TV_GDN):
+ *     S_n = alpha_n (I - beta_n k_n k_n^T) S_parent(n) + beta_n k_n v_n^T
+ *   scalar decay (mode TV_SCALAR_DECAY):
+ *     S_n = alpha_n S_parent(n) + k_n v_n^T       (alpha_n = lambda_h)
+ *   S_parent = S_root for a node whose parent is -1.
+ *   output          o_n = S_n^T q_n  (state after node n's own update)
+ *   pseudo-value    u_n = beta_n (v_n - alpha_n S_parent^T k_n)   (GDN)
+ *                   u_n = v_n                                       (scalar)
+ *   so that S_n = alpha_n S_parent + k_n u_n^T and the accepted state is
+ *   gamma_a S_root + sum_{j on path(a)} (prod of alpha after j) k_j u_j^T.
+ *
+ * Conventions for every entry point:
+ *   - Array arguments are DEVICE pointers owned by the caller; nothing is
+ *     allocated, nothing is kept between calls, calls are re-entrant.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  On success the work
+ *     is enqueued and the call returns; results are valid once the stream
+ *     reaches that point.
+ *   - The return value is host-side and synchronous: TV_OK, or a negative
+ *     TV_ERR_* code; on any error nothing is launched.  A launch failure
+ *     returns -(100 + hipError_t).
+ *   - Data errors found on the device go to status[b] (TV_STATUS_*); that
+ *     sequence's outputs are then unspecified, but no kernel reads or writes
+ *     out of bounds (bad parents are treated as -1, a bad accepted index as 0).
+ *   - Preconditions not checked: finite inputs, alpha in (0, 1]; in GDN mode
+ *     ||k_n|| <= 1 keeps (I - beta k k^T) non-expansive.
+ *   - q is used as given: an attention scale is folded in by the caller.
+ *   - N <= TV_MAX_NODES; trees of any shape up to that size are accepted.
+ */
+#ifndef TREE_VERIFY_H
+#define TREE_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_MAX_NODES 128
+
+/* dtype of q, k, v and o */
+#define TV_F32 0
+#define TV_BF16 1
+
+/* layer */
+#define TV_GDN 0
+#define TV_SCALAR_DECAY 1
+
+/* tree_verify_algo: which kernel solves the tree */
+#define TV_ALGO_AUTO 0  /* matrix-core path where it applies, else level-scheduled */
+#define TV_ALGO_LEVEL 1 /* level-scheduled forward substitution, fp32 FMA, any d */
+#define TV_ALGO_MFMA 2  /* bf16 matrix cores + per-node path solve; bf16, d_k = d_v = 128 */
+
+/* host return codes */
+#define TV_OK 0
+#define TV_ERR_NULL (-1)     /* a required pointer is NULL */
+#define TV_ERR_DIMS (-2)     /* B, H or N <= 0, N > TV_MAX_NODES, or a size overflows */
+#define TV_ERR_HEAD_DIM (-3) /* d_k or d_v not in {16, 32, 64, 128} */
+#define TV_ERR_MODE (-4)     /* bad dtype or mode, or beta == NULL in GDN mode */
+#define TV_ERR_ALIAS (-5)    /* S_out overlaps S_root without being equal to it */
+#define TV_ERR_ALGO (-6)     /* bad algo, or TV_ALGO_MFMA where it does not apply */
+#define TV_ERR_HIP_BASE (-100)
+
+/* device status codes, status[b] */
+#define TV_STATUS_OK 0
+#define TV_STATUS_BAD_PARENTS 1  /* some parents[b][i] outside [-1, i-1] */
+#define TV_STATUS_BAD_ACCEPTED 2 /* accepted[b] outside [0, N) */
+
+/*
+ * tree_verify -- outputs of all N draft nodes of B sequences x H heads in one
+ * launch, plus the pseudo-value matrix U that tree_commit needs.
+ *
+ *   q, k      [B, N, H, dk]  dtype, contiguous
+ *   v         [B, N, H, dv]  dtype, contiguous
+ *   alpha     [B, N, H] f32  decay per token (lambda_h broadcast in scalar mode)
+ *   beta      [B, N, H] f32  write strength (GDN); ignored, may be NULL, in scalar mode
+ *   parents   [B, N] int32   parents[b][i] in [-1, i-1]; -1 hangs node i off S_root
+ *   S_root    [B, H, dk, dv] f32   state before the draft tree
+ *   o         [B, N, H, dv]  OUT, dtype (bf16 is rounded to nearest even)
+ *   U         [B, H, N, dv]  OUT, f32 (U = v in scalar mode)
+ *   status    [B] int32      OUT, or NULL
+ */
+int tree_verify(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                const void* k, const void* v, const float* alpha, const float* beta,
+                const int32_t* parents, const float* S_root, void* o, float* U, int32_t* status,
+                void* stream);
+
+/* tree_verify with an explicit solver choice (TV_ALGO_*); same outputs within
+ * floating-point rounding.  Used by tests to exercise both solvers. */
+int tree_verify_algo(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                     const void* k, const void* v, const float* alpha, const float* beta,
+                     const int32_t* parents, const float* S_root, void* o, float* U,
+                     int32_t* status, int algo, int vblock, void* stream);
+
+/*
+ * tree_commit -- state after the accepted node of each sequence, from S_root
+ * and the token-level factors (k, alpha, U) of that node's root path only.
+ *
+ *   k         [B, N, H, dk]  dtype     (as passed to tree_verify)
+ *   alpha     [B, N, H] f32
+ *   U         [B, H, N, dv] f32        (from tree_verify)
+ *   parents   [B, N] int32
+ *   accepted  [B] int32      node index in [0, N)
+ *   S_root    [B, H, dk, dv] f32
+ *   S_out     [B, H, dk, dv] f32 OUT;  S_out == S_root (in place) is allowed,
+ *                                      any other overlap is TV_ERR_ALIAS
+ *   path_out  [B, N] int32   OUT or NULL: accepted node's path, root side
+ *                            first, padded with -1 (all -1 for a bad row)
+ *   status    [B] int32      OUT or NULL: 1 bad parents, else 2 bad accepted, else 0
+ * The caller keeps k, alpha, U and parents alive from tree_verify until this
+ * call's work has run.
+ */
+int tree_commit(int B, int H, int N, int dk, int dv, int dtype, const void* k, const float* alpha,
+                const float* U, const int32_t* parents, const int32_t* accepted,
+                const float* S_root, float* S_out, int32_t* path_out, int32_t* status,
+                void* stream);
+
+/*
+ * tree_index -- the tree bookkeeping both kernels do internally, exposed for
+ * bit-exact testing.
+ *   parents [B, N] int32
+ *   depth   [B, N] int32 OUT   (parent -1 -> depth 0)
+ *   anc     [B, N, (N+63)/64] uint64 OUT: bit j%64 of word j/64 set when node j
+ *           is on the root-to-n path, n included
+ *   status  [B] int32 OUT or NULL (1 bad parents; that row's depth/anc are 0)
+ */
+int tree_index(int B, int N, const int32_t* parents, int32_t* depth, uint64_t* anc,
+               int32_t* status, void* stream);
+
+/* Text for a return code (negative) or a status code (0..2). Never NULL. */
+const char* tv_status_string(int code);
+
+/* ABI version: major * 100 + minor. */
+int tv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_VERIFY_H */

@@ -1,0 +1,67 @@
+"""Helpers for GPU-vs-oracle parity: run both sides on one seeded batch, compare.
+
+Tolerances (floating point): per (sequence, head) slice, max|gpu - oracle| /
+max|oracle|, maxed over slices; a slice whose oracle values are all zero must
+come back exactly zero.  fp32 inputs: 1e-4 on o, U and the committed state.
+bf16 q/k/v: 2e-2 on o, 1e-3 on U and on the committed fp32 state.  Integer
+outputs (depth, ancestor bits, paths, status) must match exactly.
+"""
+import numpy as np
+
+import oracle
+from tree_speculative_verification_amd import synth
+
+TOL = {synth.F32: dict(o=1e-4, U=1e-4, S=1e-4),
+       synth.BF16: dict(o=2e-2, U=1e-3, S=1e-3)}
+
+
+def max_rel(x, y, b_axis, h_axis):
+    """Largest per-(b, h) normwise relative error of x against reference y."""
+    x = np.moveaxis(np.asarray(x, np.float64), (b_axis, h_axis), (0, 1))
+    y = np.moveaxis(np.asarray(y, np.float64), (b_axis, h_axis), (0, 1))
+    B, H = x.shape[:2]
+    err = np.abs(x - y).reshape(B, H, -1).max(-1)
+    ref = np.abs(y).reshape(B, H, -1).max(-1)
+    zero = ref == 0
+    if np.any(zero & (err != 0)):
+        return float("inf")
+    if np.all(zero):
+        return 0.0
+    return float((err[~zero] / ref[~zero]).max())
+
+
+def run_gpu(batch, algo=0, vblock=0, device="cuda", inplace=False):
+    """Verify then commit on the GPU; returns host numpy arrays."""
+    import torch
+
+    from tree_speculative_verification_amd import binding as tvb
+    t = synth.to_torch(batch, device)
+    o, U, st_v = tvb.verify(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["parents"],
+                            t["S_root"], mode=batch.mode, algo=algo, vblock=vblock)
+    S_in = t["S_root"].clone() if inplace else t["S_root"]
+    S_new, path, st_c = tvb.commit(t["k"], t["alpha"], U, t["parents"], t["accepted"], S_in,
+                                   inplace=inplace)
+    torch.cuda.synchronize()
+    return dict(o=o.float().cpu().numpy(), U=U.cpu().numpy(), S=S_new.cpu().numpy(),
+                path=path.cpu().numpy(), status_v=st_v.cpu().numpy(),
+                status_c=st_c.cpu().numpy())
+
+
+def run_oracle(batch):
+    o, U, st_v = oracle.verify(batch.mode, batch.parents, batch.q, batch.k, batch.v, batch.alpha,
+                               batch.beta, batch.S_root)
+    S, st_c = oracle.commit(batch.mode, batch.parents, batch.accepted, batch.k, batch.v,
+                            batch.alpha, batch.beta, batch.S_root)
+    path, st_p = oracle.accepted_paths(batch.parents, batch.accepted)
+    return dict(o=o, U=U, S=S, path=path, status_v=st_v, status_c=st_c)
+
+
+def compare(gpu, ref, dtype, rows=None):
+    """Errors of the GPU outputs; rows (a bool mask over sequences) limits the check."""
+    tol = TOL[dtype]
+    sel = slice(None) if rows is None else rows
+    errs = dict(o=max_rel(gpu["o"][sel], ref["o"][sel], 0, 2),
+                U=max_rel(gpu["U"][sel], ref["U"][sel], 0, 1),
+                S=max_rel(gpu["S"][sel], ref["S"][sel], 0, 1))
+    ok = all(errs[key] <= tol[key] for key in errs)
+    return ok, errs

@@ -1,0 +1,130 @@
+"""The C ABI library loads, exports what include/tree_verify.h declares, and
+rejects bad arguments on the host before launching anything (no GPU needed:
+every call here fails its host checks, so no device pointer is touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_verify.h")
+LIB_PATH = os.path.join(ROOT, "tree_speculative_verification_amd", "libtreeverify.so")
+
+TV_ERR_NULL, TV_ERR_DIMS, TV_ERR_HEAD_DIM, TV_ERR_MODE, TV_ERR_ALIAS, TV_ERR_ALGO = -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        from tree_speculative_verification_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB_PATH)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L.tree_verify.argtypes = [I] * 7 + [P] * 11
+    L.tree_verify_algo.argtypes = [I] * 7 + [P] * 10 + [I, I, P]
+    L.tree_commit.argtypes = [I] * 6 + [P] * 10
+    L.tree_index.argtypes = [I, I] + [P] * 5
+    L.tv_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected():
+    assert declared_functions() == sorted(["tree_verify", "tree_verify_algo", "tree_commit",
+                                           "tree_index", "tv_status_string", "tv_version"])
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_strings(lib):
+    assert lib.tv_version() == 100
+    for code in (0, 1, 2, -1, -2, -3, -4, -5, -6, -107):
+        s = lib.tv_status_string(code)
+        assert s and s.decode() != "unknown code", code
+    assert lib.tv_status_string(12345).decode() == "unknown code"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+def _verify(lib, B=1, H=1, N=4, dk=16, dv=16, dtype=0, mode=0, nulls=(), algo=0, vblock=0,
+            beta_null=False):
+    ptrs = [None if i in nulls else FAKE for i in range(10)]
+    if beta_null:
+        ptrs[4] = None
+    return lib.tree_verify_algo(B, H, N, dk, dv, dtype, mode, *ptrs, algo, vblock, None)
+
+
+def test_verify_null_pointers(lib):
+    for i in (0, 1, 2, 3, 5, 6, 7, 8):  # q k v alpha parents S_root o U
+        assert _verify(lib, nulls=(i,), B=0) == TV_ERR_NULL
+
+
+@pytest.mark.parametrize("B,H,N", [(0, 1, 4), (1, 0, 4), (1, 1, 0), (1, 1, 129), (-3, 1, 4),
+                                   (1 << 30, 1 << 20, 128)])
+def test_verify_bad_dims(lib, B, H, N):
+    assert _verify(lib, B=B, H=H, N=N) == TV_ERR_DIMS
+
+
+@pytest.mark.parametrize("dk,dv", [(8, 16), (16, 48), (256, 128), (0, 16)])
+def test_verify_bad_head_dims(lib, dk, dv):
+    assert _verify(lib, dk=dk, dv=dv) == TV_ERR_HEAD_DIM
+
+
+def test_verify_bad_mode_dtype(lib):
+    assert _verify(lib, dtype=2) == TV_ERR_MODE
+    assert _verify(lib, mode=7) == TV_ERR_MODE
+    assert _verify(lib, mode=0, beta_null=True) == TV_ERR_MODE
+
+
+def test_verify_bad_algo(lib):
+    assert _verify(lib, algo=9) == TV_ERR_ALGO
+    assert _verify(lib, algo=2, dtype=0, dk=128, dv=128) == TV_ERR_ALGO   # fp32 has no MFMA path
+    assert _verify(lib, algo=2, dtype=1, dk=64, dv=64) == TV_ERR_ALGO     # d != 128
+    assert _verify(lib, vblock=48, dtype=1, dk=128, dv=128) == TV_ERR_ALGO
+
+
+def test_commit_checks(lib):
+    P = FAKE
+    assert lib.tree_commit(1, 1, 4, 16, 16, 0, None, P, P, P, P, P, P, None, None, None) == TV_ERR_NULL
+    assert lib.tree_commit(1, 1, 4, 16, 16, 0, P, P, P, P, None, P, P, None, None, None) == TV_ERR_NULL
+    assert lib.tree_commit(1, 1, 200, 16, 16, 0, P, P, P, P, P, P, P, None, None, None) == TV_ERR_DIMS
+    assert lib.tree_commit(1, 1, 4, 16, 24, 0, P, P, P, P, P, P, P, None, None, None) == TV_ERR_HEAD_DIM
+    assert lib.tree_commit(1, 1, 4, 16, 16, 5, P, P, P, P, P, P, P, None, None, None) == TV_ERR_MODE
+    # S_out starting 4 bytes into S_root: partial overlap
+    s0 = ctypes.c_void_p(0x100000)
+    s1 = ctypes.c_void_p(0x100004)
+    assert lib.tree_commit(1, 1, 4, 16, 16, 0, P, P, P, P, P, s0, s1, None, None, None) == TV_ERR_ALIAS
+    assert lib.tree_commit(1, 1, 4, 16, 16, 0, P, P, P, P, P, s1, s0, None, None, None) == TV_ERR_ALIAS
+
+
+def test_index_checks(lib):
+    P = FAKE
+    assert lib.tree_index(1, 4, None, P, P, None, None) == TV_ERR_NULL
+    assert lib.tree_index(1, 4, P, None, P, None, None) == TV_ERR_NULL
+    assert lib.tree_index(0, 4, P, P, P, None, None) == TV_ERR_DIMS
+    assert lib.tree_index(1, 129, P, P, P, None, None) == TV_ERR_DIMS
+
+
+def test_product_path_has_no_oracle_import():
+    """The library package never reaches into the oracle (or any CPU fallback)."""
+    pkg = os.path.join(ROOT, "tree_speculative_verification_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "tree_oracle" not in text, f

@@ -1,0 +1,107 @@
+// Host side of the C ABI: argument checks, solver choice, launch.  Nothing is
+// launched unless every check passes; see include/tree_verify.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tree_verify.h"
+#include "tv_launch.h"
+
+namespace {
+
+bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Elements of the largest array stay well inside size_t and the device's
+// 64-bit addressing.
+bool sizes_ok(long long B, long long H, long long N, long long dk, long long dv) {
+  const long long big = 1LL << 40;
+  return B <= big / H && B * H <= big / N && B * H * N <= big / (dk > dv ? dk : dv) &&
+         B * H <= big / (dk * dv);
+}
+
+int hip_code(int err) { return err == 0 ? TV_OK : TV_ERR_HIP_BASE - err; }
+
+int check_common(int B, int H, int N, int dk, int dv, int dtype) {
+  if (B <= 0 || H <= 0 || N <= 0 || N > TV_MAX_NODES) return TV_ERR_DIMS;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv)) return TV_ERR_HEAD_DIM;
+  if (!sizes_ok(B, H, N, dk, dv)) return TV_ERR_DIMS;
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_MODE;
+  return TV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tree_verify_algo(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                     const void* k, const void* v, const float* alpha, const float* beta,
+                     const int32_t* parents, const float* S_root, void* o, float* U,
+                     int32_t* status, int algo, int vblock, void* stream) {
+  if (!q || !k || !v || !alpha || !parents || !S_root || !o || !U) return TV_ERR_NULL;
+  int rc = check_common(B, H, N, dk, dv, dtype);
+  if (rc) return rc;
+  if (mode != TV_GDN && mode != TV_SCALAR_DECAY) return TV_ERR_MODE;
+  if (mode == TV_GDN && !beta) return TV_ERR_MODE;
+  if (vblock != 0 && vblock != 32 && vblock != 64 && vblock != 128) return TV_ERR_ALGO;
+  const bool mfma_ok = dtype == TV_BF16 && dk == 128 && dv == 128;
+  if (algo == TV_ALGO_AUTO) algo = mfma_ok ? TV_ALGO_MFMA : TV_ALGO_LEVEL;
+  if (algo == TV_ALGO_MFMA && !mfma_ok) return TV_ERR_ALGO;
+  if (algo != TV_ALGO_MFMA && algo != TV_ALGO_LEVEL) return TV_ERR_ALGO;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int err;
+  if (algo == TV_ALGO_MFMA)
+    err = tv::launch_verify_mfma(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U,
+                                 status, vblock, st);
+  else
+    err = tv::launch_verify_level(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta, parents,
+                                  S_root, o, U, status, st);
+  return hip_code(err);
+}
+
+int tree_verify(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                const void* k, const void* v, const float* alpha, const float* beta,
+                const int32_t* parents, const float* S_root, void* o, float* U, int32_t* status,
+                void* stream) {
+  return tree_verify_algo(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta, parents, S_root, o,
+                          U, status, TV_ALGO_AUTO, 0, stream);
+}
+
+int tree_commit(int B, int H, int N, int dk, int dv, int dtype, const void* k, const float* alpha,
+                const float* U, const int32_t* parents, const int32_t* accepted,
+                const float* S_root, float* S_out, int32_t* path_out, int32_t* status,
+                void* stream) {
+  if (!k || !alpha || !U || !parents || !accepted || !S_root || !S_out) return TV_ERR_NULL;
+  int rc = check_common(B, H, N, dk, dv, dtype);
+  if (rc) return rc;
+  const uintptr_t bytes = (uintptr_t)B * H * dk * dv * sizeof(float);
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(S_root), b0 = reinterpret_cast<uintptr_t>(S_out);
+  if (a0 != b0 && a0 < b0 + bytes && b0 < a0 + bytes) return TV_ERR_ALIAS;
+  return hip_code(tv::launch_commit(B, H, N, dk, dv, dtype, k, alpha, U, parents, accepted, S_root,
+                                    S_out, path_out, status, static_cast<hipStream_t>(stream)));
+}
+
+int tree_index(int B, int N, const int32_t* parents, int32_t* depth, uint64_t* anc,
+               int32_t* status, void* stream) {
+  if (!parents || !depth || !anc) return TV_ERR_NULL;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || B > (1 << 30)) return TV_ERR_DIMS;
+  return hip_code(tv::launch_index(B, N, parents, depth, anc, status, static_cast<hipStream_t>(stream)));
+}
+
+const char* tv_status_string(int code) {
+  switch (code) {
+    case TV_OK: return "ok";
+    case TV_STATUS_BAD_PARENTS: return "status: a parent index is outside [-1, i-1]";
+    case TV_STATUS_BAD_ACCEPTED: return "status: accepted node index is outside [0, N)";
+    case TV_ERR_NULL: return "a required pointer is NULL";
+    case TV_ERR_DIMS: return "bad sizes: B, H, N must be positive, N <= 128, sizes must fit";
+    case TV_ERR_HEAD_DIM: return "d_k and d_v must be 16, 32, 64 or 128";
+    case TV_ERR_MODE: return "bad dtype or mode, or beta is NULL in gated-delta-rule mode";
+    case TV_ERR_ALIAS: return "S_out overlaps S_root without being the same buffer";
+    case TV_ERR_ALGO: return "bad solver choice or v-block width for these arguments";
+  }
+  if (code <= TV_ERR_HIP_BASE) return "HIP launch failed (code = -(100 + hipError_t))";
+  return "unknown code";
+}
+
+int tv_version(void) { return 100; }
+
+}  // extern "C"

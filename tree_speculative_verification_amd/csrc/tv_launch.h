@@ -1,0 +1,29 @@
+// Internal launchers behind the C ABI.  Each returns a hipError_t value (0 on
+// success); argument checking happens in tv_api.cpp before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tv {
+
+int launch_index(int B, int N, const int32_t* parents, int32_t* depth, uint64_t* anc,
+                 int32_t* status, hipStream_t stream);
+
+int launch_commit(int B, int H, int N, int dk, int dv, int dtype, const void* k, const float* alpha,
+                  const float* U, const int32_t* parents, const int32_t* accepted,
+                  const float* S_root, float* S_out, int32_t* path_out, int32_t* status,
+                  hipStream_t stream);
+
+int launch_verify_level(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                        const void* k, const void* v, const float* alpha, const float* beta,
+                        const int32_t* parents, const float* S_root, void* o, float* U,
+                        int32_t* status, hipStream_t stream);
+
+// bf16 q/k/v, d_k = d_v = 128 only.
+int launch_verify_mfma(int B, int H, int N, int mode, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, const int32_t* parents,
+                       const float* S_root, void* o, float* U, int32_t* status, int vblock,
+                       hipStream_t stream);
+
+}  // namespace tv

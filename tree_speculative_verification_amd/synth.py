@@ -271,3 +271,27 @@ def make_custom(parents, accepted, H, dk, dv, mode=GDN, dtype=F32, seed=0,
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     return TreeBatch(cfg=0, mode=mode, dtype=dtype, parents=parents, accepted=accepted,
                      q=q, k=k, v=v, alpha=alpha, beta=beta, S_root=S_root)
+
+
+def to_torch(batch: TreeBatch, device="cuda"):
+    """Copies a batch to `device` as the tensors the library takes.
+
+    q/k/v become float32 or bfloat16 (bit-exact: the host values are already
+    bf16-representable); beta is None in scalar-decay mode.
+    """
+    import torch
+
+    def vals(x):
+        if batch.dtype == BF16:
+            bits = bf16_bits(x).view(np.int16)
+            return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+    def f32(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
+
+    return dict(q=vals(batch.q), k=vals(batch.k), v=vals(batch.v), alpha=f32(batch.alpha),
+                beta=f32(batch.beta),
+                parents=torch.from_numpy(np.ascontiguousarray(batch.parents, np.int32)).to(device),
+                accepted=torch.from_numpy(np.ascontiguousarray(batch.accepted, np.int32)).to(device),
+                S_root=f32(batch.S_root), mode=batch.mode)
