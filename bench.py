@@ -6,16 +6,19 @@ One step = tree_verify + tree_commit over one batch of the 64-node workload
 64-node draft tree per sequence, accepted node uniform over nodes).  Inputs
 are seeded synthetic data, resident in HBM before timing starts.
 
-Timing: W warm-up steps, then K timed steps.  Inside each step the L2 and the
-256 MB Infinity Cache are flushed (a 1 GiB write) before each kernel, so each
-kernel streams its operands from HBM as it would between the rest of a model
-forward; HIP events on the launch stream time each kernel, flushes excluded.
-ms_per_step = mean verify + mean commit kernel time; value = B*N / that.
-The wall time of the whole timed region (flushes included) is reported too.
+Cold caches without flush kernels: R copies of the input set (>= 1 GB in all,
+far above the 256 MB Infinity Cache and the L2s) are used in turn.  Step i
+verifies set i mod R and commits set (i - 2) mod R, whose pseudo-values came
+from the verify two steps earlier; so every kernel streams its operands from
+HBM, as it would with the rest of a model forward between verify and commit.
+W warm-up steps, then K timed steps between one pair of HIP events on the
+launch stream (bracketed by device synchronizations).  ms_per_step is that
+time / K; value = B*N / ms_per_step.  Per-kernel durations for the roofline
+come from K back-to-back launches of each kernel alone over the same ring.
 
 Prints ONE JSON line.  Options: --steps K --warmup W --gpus 1 (only 1 is
 supported: the path runs on one GPU) --workload {3,4,5} --vblock {0,32,64,128}
---no-cpu-baseline --no-flush.
+--no-cpu-baseline.
 """
 from __future__ import annotations
 
@@ -146,7 +149,6 @@ def main(argv=None):
     ap.add_argument("--vblock", type=int, default=0, choices=[0, 32, 64, 128])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
-    ap.add_argument("--no-flush", action="store_true")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py: --gpus {a.gpus} is not supported; this path runs on one GPU "
@@ -164,77 +166,71 @@ def main(argv=None):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    t = synth.to_torch(bt, dev)
+    host = synth.to_torch(bt, "cpu")
     B, N, H, dk, dv = bt.B, bt.N, bt.H, bt.dk, bt.dv
-    o = torch.empty((B, N, H, dv), dtype=t["q"].dtype, device=dev)
-    U = torch.empty((B, H, N, dv), dtype=torch.float32, device=dev)
-    st_v = torch.empty((B,), dtype=torch.int32, device=dev)
-    S_out = torch.empty_like(t["S_root"])
-    path = torch.empty((B, N), dtype=torch.int32, device=dev)
-    st_c = torch.empty((B,), dtype=torch.int32, device=dev)
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    set_bytes = sum(x.numel() * x.element_size() for x in host.values() if torch.is_tensor(x))
+    set_bytes += B * N * H * dv * host["q"].element_size() + 2 * B * H * N * dv * 4 + B * H * dk * dv * 4
+    R = max(3, -(-(1 << 30) // set_bytes))
+    sets = []
+    for _ in range(R):
+        t = {key: (x.to(dev) if torch.is_tensor(x) else x) for key, x in host.items()}
+        t["o"] = torch.empty((B, N, H, dv), dtype=t["q"].dtype, device=dev)
+        t["U"] = torch.empty((B, H, N, dv), dtype=torch.float32, device=dev)
+        t["S_out"] = torch.empty_like(t["S_root"])
+        t["st_v"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        t["st_c"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        t["path"] = torch.empty((B, N), dtype=torch.int32, device=dev)
+        sets.append(t)
     stream = torch.cuda.current_stream()
 
-    def flush():
-        if not a.no_flush:
-            flush_buf.fill_(1.0)
-
-    def verify():
+    def verify(i):
+        t = sets[i % R]
         tvb.verify(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["parents"], t["S_root"],
-                   mode=bt.mode, vblock=a.vblock, o=o, U=U, status=st_v, stream=stream)
+                   mode=bt.mode, vblock=a.vblock, o=t["o"], U=t["U"], status=t["st_v"], stream=stream)
 
-    def commit():
-        tvb.commit(t["k"], t["alpha"], U, t["parents"], t["accepted"], t["S_root"], S_out=S_out,
-                   path_out=path, status=st_c, stream=stream)
+    def commit(i):
+        t = sets[i % R]
+        tvb.commit(t["k"], t["alpha"], t["U"], t["parents"], t["accepted"], t["S_root"],
+                   S_out=t["S_out"], path_out=t["path"], status=t["st_c"], stream=stream)
 
-    for _ in range(a.warmup):
-        flush()
-        verify()
-        flush()
-        commit()
-    torch.cuda.synchronize()
-    if st_v.any().item() or st_c.any().item():
-        raise RuntimeError("device status reported bad input rows")
+    def timed(body, k):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(k):
+            body(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k, (time.perf_counter() - w0) / k * 1e3
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    for i in range(R):          # every set gets pseudo-values before its first commit
+        verify(i)
+    for i in range(a.warmup):
+        verify(i)
+        commit(i - 2)
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for i in range(a.steps):
-        flush()
-        ev[i][0].record(stream)
-        verify()
-        ev[i][1].record(stream)
-        flush()
-        ev[i][2].record(stream)
-        commit()
-        ev[i][3].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    tv = np.array([e[0].elapsed_time(e[1]) for e in ev])   # ms
-    tc = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    for t in sets:
+        if t["st_v"].any().item() or t["st_c"].any().item():
+            raise RuntimeError("device status reported bad input rows")
 
-    # back-to-back without flushes (caches may hold operands): secondary figure
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(a.steps):
-        verify()
-        commit()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    warm_ms = e0.elapsed_time(e1) / a.steps
+    def step(i):
+        verify(i)
+        commit(i - 2)
 
-    ms_step = float(tv.mean() + tc.mean())
+    ms_step, wall_ms = timed(step, a.steps)
+    tv_ms, _ = timed(verify, a.steps)
+    tc_ms, _ = timed(commit, a.steps)
+
     value = B * N / (ms_step * 1e-3)
     vbytes, cbytes, L = algorithmic_bytes(bt)
     kern = {}
-    for name, ms, nbytes in (("verify", tv.mean(), vbytes), ("commit", tc.mean(), cbytes)):
+    for name, ms, nbytes in (("verify", tv_ms, vbytes), ("commit", tc_ms, cbytes)):
         gbs = nbytes / (ms * 1e-3) / 1e9
-        kern[name] = {"mean_us": round(ms * 1e3, 2), "median_us": round(float(np.median(tv if name == "verify" else tc)) * 1e3, 2),
-                      "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
+        kern[name] = {"mean_us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
                       "frac": round(gbs / HBM_PEAK_GBS, 4),
                       "traffic": measured_traffic(name, a.workload)}
-    dom = "verify" if tv.mean() >= tc.mean() else "commit"
+    dom = "verify" if tv_ms >= tc_ms else "commit"
     combined_gbs = (vbytes + cbytes) / (ms_step * 1e-3) / 1e9
     snap = B * H * N * dk * dv * 4
     u_only = B * H * N * dv * 4
@@ -247,9 +243,9 @@ def main(argv=None):
         "config": {"workload": synth.CONFIG_NAMES[a.workload], "B": B, "H": H, "N": N,
                    "d_k": dk, "d_v": dv, "qkv": "bf16", "state": "fp32", "layer": "gated delta rule",
                    "mean_path_len": round(float(L.mean()), 3), "vblock": a.vblock or "auto",
-                   "timing": "HIP events per kernel on the launch stream, L2+MALL flushed "
-                             "before each kernel (flush excluded)" if not a.no_flush else
-                             "HIP events per kernel, no flush"},
+                   "timing": f"HIP events around K steps on the launch stream; ring of {R} input "
+                             "copies (>= 1 GB) so every kernel reads cold data; commit lags verify "
+                             "by 2 steps"},
         "roofline": {"bound": "hbm", "achieved": kern[dom]["achieved_GBs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kern[dom]["frac"], "traffic": kern[dom]["traffic"],
                      "kernel": dom},
@@ -257,8 +253,7 @@ def main(argv=None):
         "verify_plus_commit": {"achieved_GBs": round(combined_gbs, 1),
                                "frac": round(combined_gbs / HBM_PEAK_GBS, 4),
                                "algorithmic_bytes": vbytes + cbytes},
-        "wall_ms_per_step_incl_flush": round(wall * 1e3 / a.steps, 4),
-        "warm_ms_per_step_no_flush": round(warm_ms, 5),
+        "wall_ms_per_step": round(wall_ms, 5),
         "transient_state_bytes": {"per_node_snapshots": snap, "U_only": u_only,
                                   "U_plus_K_and_gates": u_k_g,
                                   "ratio_snapshots_to_U": round(snap / u_only, 2),

@@ -15,6 +15,11 @@
 #include "tv_device.h"
 #include "tv_launch.h"
 
+// State rows each thread streams per tile (tile = 256 / (d_v / 4) * this rows).
+#ifndef TV_COMMIT_ROWS_PER_THREAD
+#define TV_COMMIT_ROWS_PER_THREAD 4
+#endif
+
 namespace tv {
 
 __global__ __launch_bounds__(kThreads) void index_kernel(int N, const int32_t* __restrict__ parents,
@@ -64,17 +69,22 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   const int cg = tid % CG;
   const int rsub = tid / CG;
 
-  // State loads first: their latency hides behind the path work below.
+  // Small loads first (parents, gates of every node, accepted index: the path
+  // is not known yet), then the state stream; loads retire in order, so the
+  // tree build waits only for the small ones.
+  const int pn = tid < N ? tid : N - 1;
+  const int par_v = parents[(size_t)b * N + pn];
+  const float a_all = alpha[(size_t)(b * N + pn) * H + h];
+  int a = accepted[b];
   const float4* Sp = reinterpret_cast<const float4*>(S_root + (size_t)bh * dk * DV);
   float4 s[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    const int r = r0 + rsub + p * RPP;
-    s[p] = r < dk ? Sp[(size_t)r * CG + cg] : f4(0.f);
+    const int r = min(r0 + rsub + p * RPP, dk - 1);
+    s[p] = Sp[(size_t)r * CG + cg];
   }
-
-  build_tree(t, parents + (size_t)b * N, N);
-  int a = accepted[b];
+  build_tree_from(t, par_v, N);
+  if (tid < N) al[tid] = a_all;
   const bool bad_acc = a < 0 || a >= N;
   if (bad_acc) a = 0;
   const int L = t.depth[a] + 1;
@@ -85,16 +95,15 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
     if (tid == 0 && status) status[b] = t.bad ? 1 : (bad_acc ? 2 : 0);
     if (path_out && tid < N) path_out[(size_t)b * N + tid] = (!badrow && tid < L) ? pidx[tid] : -1;
   }
-  if (tid < L) al[tid] = alpha[(size_t)(b * N + pidx[tid]) * H + h];
-  __syncthreads();
+  // coef[i] = D(path[i] -> a): product of alpha over the path nodes after path[i]
   if (tid < L) {
     float c = 1.f;
-    for (int m = tid + 1; m < L; ++m) c *= al[m];
+    for (int m = tid + 1; m < L; ++m) c *= al[pidx[m]];
     coef[tid] = c;
   }
   if (tid == 0) {
     float g = 1.f;
-    for (int m = 0; m < L; ++m) g *= al[m];
+    for (int m = 0; m < L; ++m) g *= al[pidx[m]];
     gam = g;
   }
   __syncthreads();
@@ -146,7 +155,7 @@ template <typename TK, int DV>
 static int commit_dv(int B, int H, int N, int dk, const void* k, const float* alpha, const float* U,
                      const int32_t* parents, const int32_t* accepted, const float* S_root,
                      float* S_out, int32_t* path_out, int32_t* status, hipStream_t stream) {
-  constexpr int P = 4;
+  constexpr int P = TV_COMMIT_ROWS_PER_THREAD;
   constexpr int RT = (kThreads / (DV / 4)) * P;
   const int ntiles = (dk + RT - 1) / RT;
   const long long nblocks = (long long)B * H * ntiles;

@@ -111,8 +111,10 @@ __device__ __forceinline__ int anc_rank(const TreeLds& t, int n, int j) {
 // Builds par/depth/anc for one sequence by pointer jumping: after round r each
 // node's set holds its 2^r nearest path nodes, so ceil(log2(depth+1)) rounds
 // suffice.  Invalid parents are clamped to -1 and flagged.  Every thread of
-// the block must call this; N <= kMaxNodes <= blockDim.x.
-__device__ inline void build_tree(TreeLds& t, const int32_t* __restrict__ parents_b, int N) {
+// the block must call this; N <= kMaxNodes <= blockDim.x.  `par_tid` is
+// parents_b[threadIdx.x] for threads below N (loaded by the caller, so the
+// load can be issued ahead of bulk traffic), ignored above.
+__device__ inline void build_tree_from(TreeLds& t, int par_tid, int N) {
   const int tid = threadIdx.x;
   if (tid == 0) {
     t.bad = 0;
@@ -120,7 +122,7 @@ __device__ inline void build_tree(TreeLds& t, const int32_t* __restrict__ parent
   }
   __syncthreads();
   if (tid < N) {
-    int p = parents_b[tid];
+    int p = par_tid;
     if (p < -1 || p >= tid) {
       atomicOr(&t.bad, 1);
       p = -1;
@@ -156,6 +158,11 @@ __device__ inline void build_tree(TreeLds& t, const int32_t* __restrict__ parent
     atomicMax(&t.maxdepth, d);
   }
   __syncthreads();
+}
+
+__device__ inline void build_tree(TreeLds& t, const int32_t* __restrict__ parents_b, int N) {
+  const int tid = threadIdx.x;
+  build_tree_from(t, parents_b[tid < N ? tid : 0], N);
 }
 
 // ------------------------------------------------- level-scheduled tree solve
