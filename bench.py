@@ -17,8 +17,7 @@ time / K; value = B*N / ms_per_step.  Per-kernel durations for the roofline
 come from K back-to-back launches of each kernel alone over the same ring.
 
 Prints ONE JSON line.  Options: --steps K --warmup W --gpus 1 (only 1 is
-supported: the path runs on one GPU) --workload {3,4,5} --vblock {0,32,64,128}
---no-cpu-baseline.
+supported: the path runs on one GPU) --workload {3,4,5} --no-cpu-baseline.
 """
 from __future__ import annotations
 
@@ -146,7 +145,6 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5])
-    ap.add_argument("--vblock", type=int, default=0, choices=[0, 32, 64, 128])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     a = ap.parse_args(argv)
@@ -186,7 +184,7 @@ def main(argv=None):
     def verify(i):
         t = sets[i % R]
         tvb.verify(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["parents"], t["S_root"],
-                   mode=bt.mode, vblock=a.vblock, o=t["o"], U=t["U"], status=t["st_v"], stream=stream)
+                   mode=bt.mode, o=t["o"], U=t["U"], status=t["st_v"], stream=stream)
 
     def commit(i):
         t = sets[i % R]
@@ -242,7 +240,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[a.workload], "B": B, "H": H, "N": N,
                    "d_k": dk, "d_v": dv, "qkv": "bf16", "state": "fp32", "layer": "gated delta rule",
-                   "mean_path_len": round(float(L.mean()), 3), "vblock": a.vblock or "auto",
+                   "mean_path_len": round(float(L.mean()), 3),
                    "timing": f"HIP events around K steps on the launch stream; ring of {R} input "
                              "copies (>= 1 GB) so every kernel reads cold data; commit lags verify "
                              "by 2 steps"},

@@ -110,7 +110,7 @@ int tree_verify(int B, int H, int N, int dk, int dv, int dtype, int mode, const 
 int tree_verify_algo(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
                      const void* k, const void* v, const float* alpha, const float* beta,
                      const int32_t* parents, const float* S_root, void* o, float* U,
-                     int32_t* status, int algo, int vblock, void* stream);
+                     int32_t* status, int algo, void* stream);
 
 /*
  * tree_commit -- state after the accepted node of each sequence, from S_root

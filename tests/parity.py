@@ -30,14 +30,14 @@ def max_rel(x, y, b_axis, h_axis):
     return float((err[~zero] / ref[~zero]).max())
 
 
-def run_gpu(batch, algo=0, vblock=0, device="cuda", inplace=False):
+def run_gpu(batch, algo=0, device="cuda", inplace=False):
     """Verify then commit on the GPU; returns host numpy arrays."""
     import torch
 
     from tree_speculative_verification_amd import binding as tvb
     t = synth.to_torch(batch, device)
     o, U, st_v = tvb.verify(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["parents"],
-                            t["S_root"], mode=batch.mode, algo=algo, vblock=vblock)
+                            t["S_root"], mode=batch.mode, algo=algo)
     S_in = t["S_root"].clone() if inplace else t["S_root"]
     S_new, path, st_c = tvb.commit(t["k"], t["alpha"], U, t["parents"], t["accepted"], S_in,
                                    inplace=inplace)

@@ -23,7 +23,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P, I = ctypes.c_void_p, ctypes.c_int
     L.tree_verify.argtypes = [I] * 7 + [P] * 11
-    L.tree_verify_algo.argtypes = [I] * 7 + [P] * 10 + [I, I, P]
+    L.tree_verify_algo.argtypes = [I] * 7 + [P] * 10 + [I, P]
     L.tree_commit.argtypes = [I] * 6 + [P] * 10
     L.tree_index.argtypes = [I, I] + [P] * 5
     L.tv_status_string.restype = ctypes.c_char_p
@@ -60,12 +60,12 @@ def test_version_and_strings(lib):
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
 
 
-def _verify(lib, B=1, H=1, N=4, dk=16, dv=16, dtype=0, mode=0, nulls=(), algo=0, vblock=0,
+def _verify(lib, B=1, H=1, N=4, dk=16, dv=16, dtype=0, mode=0, nulls=(), algo=0,
             beta_null=False):
     ptrs = [None if i in nulls else FAKE for i in range(10)]
     if beta_null:
         ptrs[4] = None
-    return lib.tree_verify_algo(B, H, N, dk, dv, dtype, mode, *ptrs, algo, vblock, None)
+    return lib.tree_verify_algo(B, H, N, dk, dv, dtype, mode, *ptrs, algo, None)
 
 
 def test_verify_null_pointers(lib):
@@ -94,7 +94,7 @@ def test_verify_bad_algo(lib):
     assert _verify(lib, algo=9) == TV_ERR_ALGO
     assert _verify(lib, algo=2, dtype=0, dk=128, dv=128) == TV_ERR_ALGO   # fp32 has no MFMA path
     assert _verify(lib, algo=2, dtype=1, dk=64, dv=64) == TV_ERR_ALGO     # d != 128
-    assert _verify(lib, vblock=48, dtype=1, dk=128, dv=128) == TV_ERR_ALGO
+    assert _verify(lib, algo=-1) == TV_ERR_ALGO
 
 
 def test_commit_checks(lib):

@@ -88,12 +88,11 @@ def _sampled(cfg, nb, nh, seed):
     return bt, bs, hs
 
 
-@pytest.mark.parametrize("cfg,algo,vblock", [(4, 0, 0), (4, MFMA, 32), (4, MFMA, 128),
-                                             (4, LEVEL, 0), (5, 0, 0)])
-def test_full_size_sampled(cfg, algo, vblock):
+@pytest.mark.parametrize("cfg,algo", [(4, 0), (4, LEVEL), (5, 0)])
+def test_full_size_sampled(cfg, algo):
     """Full-size launch (as the benchmark runs it); oracle on sampled (sequence, head) slices."""
     bt, bs, hs = _sampled(cfg, 4, 3, seed=cfg * 10 + algo)
-    gpu = run_gpu(bt, algo=algo, vblock=vblock)
+    gpu = run_gpu(bt, algo=algo)
     sub = bt.select(bs, hs)
     ref = run_oracle(sub)
     g = dict(o=gpu["o"][bs][:, :, hs], U=gpu["U"][bs][:, hs], S=gpu["S"][bs][:, hs])
@@ -224,12 +223,18 @@ def test_repeat_runs_bitwise_identical():
         assert np.array_equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("vblock", [32, 64, 128])
-def test_vblock_widths_agree(vblock):
-    bt = cfg_batch(4).select(np.arange(4), np.arange(16))
-    gpu = run_gpu(bt, algo=MFMA, vblock=vblock)
+@pytest.mark.parametrize("N", [8, 32, 40, 64, 96, 128])
+def test_node_tile_shapes_agree_with_level_solver(N):
+    """Each node-count bucket of the matrix-core kernel against the level-scheduled
+    kernel and the oracle on the same inputs."""
+    rng = np.random.default_rng(100 + N)
+    par = _random_parents(rng, 2, N, "random")
+    bt = _custom(par, np.array([N - 1, N // 3], np.int32), H=4, seed=N)
+    a = run_gpu(bt, algo=MFMA)
+    b = run_gpu(bt, algo=LEVEL)
     ref = run_oracle(bt)
-    _check(bt, gpu, ref)
+    _check(bt, a, ref)
+    _check(bt, b, ref)
 
 
 def test_commit_alone_with_oracle_pseudo_values():

@@ -38,7 +38,7 @@ def _load() -> ctypes.CDLL:
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.tree_verify.argtypes = [I] * 7 + [P] * 10 + [P]
     lib.tree_verify.restype = I
-    lib.tree_verify_algo.argtypes = [I] * 7 + [P] * 10 + [I, I, P]
+    lib.tree_verify_algo.argtypes = [I] * 7 + [P] * 10 + [I, P]
     lib.tree_verify_algo.restype = I
     lib.tree_commit.argtypes = [I] * 6 + [P] * 9 + [P]
     lib.tree_commit.restype = I
@@ -89,7 +89,7 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def verify(q, k, v, alpha, beta, parents, S_root, mode=TV_GDN, algo=TV_ALGO_AUTO, vblock=0,
+def verify(q, k, v, alpha, beta, parents, S_root, mode=TV_GDN, algo=TV_ALGO_AUTO,
            o=None, U=None, status=None, stream=None):
     """Per-node outputs o [B,N,H,dv] (q's dtype), pseudo-values U [B,H,N,dv] f32, status [B] i32."""
     B, N, H, dk = q.shape
@@ -115,7 +115,7 @@ def verify(q, k, v, alpha, beta, parents, S_root, mode=TV_GDN, algo=TV_ALGO_AUTO
     _check(status, "status", (B,), torch.int32, dev)
     rc = LIB.tree_verify_algo(B, H, N, dk, dv, _dtype_code(q), mode, _ptr(q), _ptr(k), _ptr(v),
                               _ptr(alpha), _ptr(beta), _ptr(parents), _ptr(S_root), _ptr(o),
-                              _ptr(U), _ptr(status), algo, vblock, _stream(stream))
+                              _ptr(U), _ptr(status), algo, _stream(stream))
     if rc != 0:
         raise TreeVerifyError(rc, "tree_verify")
     return o, U, status

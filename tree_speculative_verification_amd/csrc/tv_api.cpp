@@ -35,13 +35,12 @@ extern "C" {
 int tree_verify_algo(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
                      const void* k, const void* v, const float* alpha, const float* beta,
                      const int32_t* parents, const float* S_root, void* o, float* U,
-                     int32_t* status, int algo, int vblock, void* stream) {
+                     int32_t* status, int algo, void* stream) {
   if (!q || !k || !v || !alpha || !parents || !S_root || !o || !U) return TV_ERR_NULL;
   int rc = check_common(B, H, N, dk, dv, dtype);
   if (rc) return rc;
   if (mode != TV_GDN && mode != TV_SCALAR_DECAY) return TV_ERR_MODE;
   if (mode == TV_GDN && !beta) return TV_ERR_MODE;
-  if (vblock != 0 && vblock != 32 && vblock != 64 && vblock != 128) return TV_ERR_ALGO;
   const bool mfma_ok = dtype == TV_BF16 && dk == 128 && dv == 128;
   if (algo == TV_ALGO_AUTO) algo = mfma_ok ? TV_ALGO_MFMA : TV_ALGO_LEVEL;
   if (algo == TV_ALGO_MFMA && !mfma_ok) return TV_ERR_ALGO;
@@ -50,7 +49,7 @@ int tree_verify_algo(int B, int H, int N, int dk, int dv, int dtype, int mode, c
   int err;
   if (algo == TV_ALGO_MFMA)
     err = tv::launch_verify_mfma(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U,
-                                 status, vblock, st);
+                                 status, st);
   else
     err = tv::launch_verify_level(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta, parents,
                                   S_root, o, U, status, st);
@@ -62,7 +61,7 @@ int tree_verify(int B, int H, int N, int dk, int dv, int dtype, int mode, const 
                 const int32_t* parents, const float* S_root, void* o, float* U, int32_t* status,
                 void* stream) {
   return tree_verify_algo(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta, parents, S_root, o,
-                          U, status, TV_ALGO_AUTO, 0, stream);
+                          U, status, TV_ALGO_AUTO, stream);
 }
 
 int tree_commit(int B, int H, int N, int dk, int dv, int dtype, const void* k, const float* alpha,
@@ -96,7 +95,7 @@ const char* tv_status_string(int code) {
     case TV_ERR_HEAD_DIM: return "d_k and d_v must be 16, 32, 64 or 128";
     case TV_ERR_MODE: return "bad dtype or mode, or beta is NULL in gated-delta-rule mode";
     case TV_ERR_ALIAS: return "S_out overlaps S_root without being the same buffer";
-    case TV_ERR_ALGO: return "bad solver choice or v-block width for these arguments";
+    case TV_ERR_ALGO: return "bad solver choice for these arguments";
   }
   if (code <= TV_ERR_HIP_BASE) return "HIP launch failed (code = -(100 + hipError_t))";
   return "unknown code";

@@ -23,7 +23,7 @@ int launch_verify_level(int B, int H, int N, int dk, int dv, int dtype, int mode
 // bf16 q/k/v, d_k = d_v = 128 only.
 int launch_verify_mfma(int B, int H, int N, int mode, const void* q, const void* k, const void* v,
                        const float* alpha, const float* beta, const int32_t* parents,
-                       const float* S_root, void* o, float* U, int32_t* status, int vblock,
+                       const float* S_root, void* o, float* U, int32_t* status,
                        hipStream_t stream);
 
 }  // namespace tv

@@ -17,23 +17,27 @@
 // o_n = gamma_n QS_n + w.R_path with x, w from one backward substitution of
 // length len(n) (x for e_last, w for the read-out row).
 //
-// One workgroup per (b, h, block of VB value columns), four waves:
+// One workgroup per (b, h, block of VB value columns); four waves, wave w owns
+// node tile w / CT and value-column tile w % CT (NT * CT = 4):
 //   1. loads, small ones first: parents and gates, K and Q rows (staged in
-//      LDS), this wave's 32 columns of S_root straight into MFMA operand
+//      LDS), the wave's 32 columns of S_root straight into MFMA operand
 //      registers, and V at the positions the outputs land on;
-//   2. tree index by pointer jumping: depth and ancestor bitsets in LDS;
-//   3. Gram on matrix cores (32x32x16 bf16, exact products): lower-triangular
-//      blocks of K K^T and Q K^T; only ancestor-pair entries are kept,
-//      stored by the ancestor's depth (the ancestor-masked Gram/decay builder);
-//   4. one thread per node solves its path for x and w (decays as running
-//      products of alpha, no log/exp), padded with zeros to 16 entries;
-//      this overlaps the S stream;
+//   2. tree index in registers, one copy per wave: pointer jumping over the
+//      parent array with cross-lane shuffles gives each node's ancestor bitset
+//      and, in the same pass, gamma (product of alpha over the path);
+//   3. Gram on matrix cores (32x32x16 bf16, exact products), transposed so a
+//      lane owns a node: lower-triangular blocks of K K^T and K Q^T; a lane
+//      keeps the entries whose row is on its node's path, stored by that
+//      ancestor's depth (the ancestor-masked Gram/decay builder);
+//   4. each lane solves the path of the node it will output (x for U, w for
+//      o; decays as running products of alpha, no log/exp); the coefficients
+//      stay in registers; this overlaps the S stream;
 //   5. Y^T = S_block^T [K;Q]^T on matrix cores with S split into bf16 hi + lo
 //      (q and k are exact in bf16: ~2^-17 relative error); the accumulator
 //      layout puts one node and 16 value columns in each lane;
 //   6. R = beta (V - gamma KS) from the K accumulators into LDS;
-//   7. U and o gathered over each node's path rows of R (float4), o starting
-//      from gamma_n QS_n in the Q accumulators; stored straight to HBM.
+//   7. U and o gathered over the node's path rows of R (float4 loads),
+//      o starting from gamma_n QS_n in the Q accumulators; stored to HBM.
 // Trees with a path longer than 16 take the level-scheduled solve instead
 // (same kernel, same outputs).
 #include "tv_device.h"
@@ -54,11 +58,12 @@ struct MfmaLayout {
   static constexpr int stage = 2 * NP * kRow * 2;   // K, Q bf16 until the Y contraction
   static constexpr int rbytes = NP * RS * 4;        // R rows, over the dead staging
   static constexpr int u0 = stage > rbytes ? stage : rbytes;
-  static constexpr int bytes = u0 > (int)sizeof(LevelLds) ? u0 : (int)sizeof(LevelLds);
+  static constexpr int fb = (int)(sizeof(LevelLds) + sizeof(TreeLds));  // level-scheduled fallback
+  static constexpr int bytes = u0 > fb ? u0 : fb;
 };
 
 // Accumulator element r of a 32x32 tile sits at row 8*(r/4) + 4*(lane/32) + r%4,
-// column lane%32.  In Y^T the rows are value columns and the columns are nodes.
+// column lane%32.  In Y^T and G^T the columns are nodes.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 __device__ __forceinline__ float4 bf16x4_to_f32(uint2 u) {
@@ -73,8 +78,96 @@ __device__ __forceinline__ uint2 f32x4_to_bf16(float a, float b, float c, float 
   return r;
 }
 
+// ---- tree index in registers (lane l holds node l, and node l + 64 when SL = 2) ----
+
+template <int SL>
+struct WaveTree {
+  unsigned long long a0[SL], a1[SL];  // inclusive ancestor bitsets, nodes 0..63 and 64..127
+  float g[SL];                        // gamma: product of alpha over the root path
+};
+
+// Value of a per-node register for node j (owned by lane j % 64, slot j / 64).
+template <int SL, typename T>
+__device__ __forceinline__ T node_val(const T (&x)[SL], int j) {
+  const int src = j & 63;
+  T v = __shfl(x[0], src);
+  if constexpr (SL == 2) {
+    const T v1 = __shfl(x[1], src);
+    v = j >= 64 ? v1 : v;
+  }
+  return v;
+}
+
+// Pointer jumping: each round a node adopts the span of the node its jump
+// pointer names (ancestor set, product of alpha) and jumps past it, so spans
+// double until every jump pointer runs off the root.  Spans stay contiguous
+// path segments whether or not the named node already moved this round.
+// Returns the tree's longest path length (same in every wave) and flags
+// parents outside [-1, i-1] (treated as -1).
+template <int SL>
+__device__ void wave_tree(WaveTree<SL>& T, const int (&par)[SL], const float (&al)[SL], int N,
+                          bool& bad, int& Lmax) {
+  const int lane = threadIdx.x & 63;
+  int jp[SL];
+  bool badl = false;
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    const int node = lane + 64 * s;
+    int p = par[s];
+    if (node < N && (p < -1 || p >= node)) {
+      badl = true;
+      p = -1;
+    }
+    jp[s] = node < N ? p : -1;
+    T.a0[s] = node < 64 ? (1ull << node) : 0ull;
+    T.a1[s] = node < 64 ? 0ull : (1ull << (node - 64));
+    T.g[s] = node < N ? al[s] : 1.f;
+  }
+  while (true) {
+    bool act = false;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) act |= jp[s] >= 0;
+    if (!__any(act)) break;
+    unsigned long long x0[SL], x1[SL];
+    float xg[SL];
+    int xj[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int j = jp[s] >= 0 ? jp[s] : 0;
+      x0[s] = node_val<SL>(T.a0, j);
+      x1[s] = node_val<SL>(T.a1, j);
+      xg[s] = node_val<SL>(T.g, j);
+      xj[s] = node_val<SL>(jp, j);
+    }
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      if (jp[s] >= 0) {
+        T.a0[s] |= x0[s];
+        T.a1[s] |= x1[s];
+        T.g[s] *= xg[s];
+        jp[s] = xj[s];
+      }
+    }
+  }
+  int L = 0;
+#pragma unroll
+  for (int s = 0; s < SL; ++s)
+    if (lane + 64 * s < N) L = max(L, __popcll(T.a0[s]) + __popcll(T.a1[s]));
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) L = max(L, __shfl_xor(L, m));
+  Lmax = L;
+  bad = __any(badl);
+}
+
+// Position of node j on the root path whose set is (a0, a1) = number of path
+// nodes with a smaller index = depth of j when j is on that path.
+__device__ __forceinline__ int rank_below(unsigned long long a0, unsigned long long a1, int j) {
+  if (j < 64) return __popcll(a0 & ((1ull << j) - 1ull));
+  return __popcll(a0) + __popcll(a1 & ((1ull << (j - 64)) - 1ull));
+}
+
 template <int NP, int VB>
-__global__ __launch_bounds__(kThreads) void verify_mfma_kernel(
+__global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     int H, int N, int mode, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const int32_t* __restrict__ parents,
@@ -83,26 +176,32 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(
   using Lay = MfmaLayout<NP, VB>;
   constexpr int NT = NP / 32;                 // node tiles
   constexpr int CT = VB / 32;                 // value-column tiles in the block
+  static_assert(NT * CT == 4, "one (node tile, column tile) pair per wave");
   constexpr int NVB = kD / VB;
-  constexpr int PAIRS = NT * CT;              // (node tile, column tile) output tiles
-  static_assert(PAIRS % 4 == 0, "four waves share the output tiles evenly");
-  constexpr int PPW = PAIRS / 4;
-  constexpr int NG = NT * (NT + 1);           // lower-triangular blocks of K K^T and Q K^T
+  constexpr int SL = NP > 64 ? 2 : 1;         // tree nodes per lane
+  constexpr int NG = NT * (NT + 1);           // lower-triangular blocks of K K^T and K Q^T
   constexpr int GPW = (NG + 3) / 4;
   constexpr int KQPT = 2 * NP * (kD / 8) / kThreads;  // 16-byte chunks of K and Q per thread
   constexpr int RS = Lay::RS;
 
   __shared__ __align__(16) unsigned char smem[Lay::bytes];
-  __shared__ float Ckk[NP * kMaxL], Cqk[NP * kMaxL];   // ancestor Gram entries by depth
-  __shared__ __align__(8) float2 XW[NP * kMaxL];       // path coefficients (x for U, w for o)
-  __shared__ uint8_t Ep[NP * kMaxL];                   // path nodes, distance order
-  __shared__ TreeLds t;
+  // Per-node tables are stored [index][node] so lanes that touch different
+  // nodes at one index hit consecutive banks.
+  // Path Gram entries by distance: CkkD[d][m] = k_m . k_j, CqkD[d][m] = q_m . k_j
+  // for the ancestor j of node m that sits d steps above m (d = 0: m itself).
+  __shared__ __align__(16) float CkkD[kMaxL * NP];
+  __shared__ __align__(16) float CqkD[kMaxL * NP];
+  __shared__ float gsink[64];                          // Gram entries off every path land here
+  __shared__ __align__(16) float2 XWT[kMaxL * NP];     // path coefficients [distance][node] (x for U, w for o)
+  __shared__ __align__(16) uint8_t Ep[NP * kMaxL];     // path nodes [node][distance]
+  __shared__ __align__(16) unsigned long long anc_s[NP][2];
   __shared__ float sal[NP], sbe[NP], sga[NP];
-  __shared__ int Lsh[NP];
+  __shared__ int meta[2];                              // longest path, bad-parents flag
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lm = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: wave-uniform branches
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int vb = bid % NVB;
   const int bh = bid / NVB;
@@ -110,18 +209,27 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(
   const int b = bh / H;
   const int cbase = vb * VB;
   const bool gdn = mode == kGdn;
-  const int ct_w = wave % CT;                 // every tile of this wave uses this column tile
-  const int col0 = ct_w * 32 + 4 * (lane >> 5);   // + 8 g + j: this lane's columns in the block
-  const int arow = lane & 31;
+  const int nt_w = wave / CT;                  // this wave's node tile
+  const int ct_w = wave % CT;                  // this wave's column tile
   const int akof = 8 * (lane >> 5);
+  const int col0 = ct_w * 32 + 4 * (lane >> 5);   // + 8 g + j: this lane's columns in the block
+  const int my_n0 = nt_w * 32 + lm;            // node this lane outputs
+  const int my_n = min(my_n0, N - 1);
 
   // ---- 1. loads: small ones first (loads retire in order) ----
   // Row indices are clamped, not branched on: padded rows repeat row N-1 and
   // only feed outputs that are discarded.
-  const int pn = tid < N ? tid : N - 1;
-  const int par_v = parents[(size_t)b * N + pn];
-  const float a_n = alpha[(size_t)(b * N + pn) * H + h];
-  const float b_raw = (gdn ? beta : alpha)[(size_t)(b * N + pn) * H + h];
+  int par[SL];
+  float al[SL], be[SL];
+  if (wave == 0) {
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int nd = min(lane + 64 * s, N - 1);
+      par[s] = parents[(size_t)b * N + nd];
+      al[s] = alpha[(size_t)(b * N + nd) * H + h];
+      be[s] = (gdn ? beta : alpha)[(size_t)(b * N + nd) * H + h];
+    }
+  }
   uint4 kq[KQPT];
 #pragma unroll
   for (int i = 0; i < KQPT; ++i) {
@@ -134,22 +242,18 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(
   }
   float sv[8][8];
   {
-    const float* Sb = S_root + (size_t)bh * kD * kD + cbase + ct_w * 32 + (lane & 31);
+    const float* Sb = S_root + (size_t)bh * kD * kD + cbase + ct_w * 32 + lm;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int i = 0; i < 8; ++i) sv[ks][i] = Sb[(size_t)(ks * 16 + akof + i) * kD];
   }
-  uint2 vv[PPW][4];
+  uint2 vv[4];
+  {
+    const uint16_t* vr = v + ((size_t)(b * N + my_n) * H + h) * kD + cbase + col0;
 #pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    const int nt = (wave + 4 * pi) / CT;
-    const int n = min(nt * 32 + arow, N - 1);
-    const uint16_t* vr = v + ((size_t)(b * N + n) * H + h) * kD + cbase + col0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) vv[pi][g] = *reinterpret_cast<const uint2*>(vr + 8 * g);
+    for (int g = 0; g < 4; ++g) vv[g] = *reinterpret_cast<const uint2*>(vr + 8 * g);
   }
-  const float b_n = gdn ? b_raw : 0.f;
   uint16_t* Ksh = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Qsh = Ksh + NP * kRow;
 #pragma unroll
@@ -160,237 +264,294 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(
     const int ch = c & 15;
     *reinterpret_cast<uint4*>((which ? Qsh : Ksh) + row * kRow + ch * 8) = kq[i];
   }
-  if (tid < N) {
-    sal[tid] = a_n;
-    sbe[tid] = b_n;
-  }
 
-  // ---- 2. tree index ----
-  build_tree_from(t, par_v, N);
-  if (h == 0 && vb == 0 && tid == 0 && status) status[b] = t.bad ? 1 : 0;
-  if (t.maxdepth + 1 > kMaxL) {
-    level_solve<uint16_t>(t, *reinterpret_cast<LevelLds*>(smem), mode, b, h, H, N, kD, kD, cbase,
+  // ---- 2. tree index: wave 0, in registers, then to LDS ----
+  if (wave == 0) {
+    WaveTree<SL> T;
+    bool bad;
+    int Lmax;
+    wave_tree<SL>(T, par, al, N, bad, Lmax);
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int nd = lane + 64 * s;
+      if (nd < NP) {
+        anc_s[nd][0] = T.a0[s];
+        anc_s[nd][1] = T.a1[s];
+        sga[nd] = T.g[s];
+        sal[nd] = al[s];
+        sbe[nd] = gdn ? be[s] : 0.f;
+      }
+    }
+    if (lane == 0) {
+      meta[0] = Lmax;
+      meta[1] = bad;
+    }
+  }
+  __syncthreads();  // tree, gates and K/Q staging visible
+  const int Lmax = __builtin_amdgcn_readfirstlane(meta[0]);  // uniform: scalar loop bounds
+  if (h == 0 && vb == 0 && tid == 0 && status) status[b] = meta[1] ? 1 : 0;
+  if (Lmax > kMaxL) {
+    __syncthreads();  // the staging area becomes the fallback's tables
+    TreeLds& tfb = *reinterpret_cast<TreeLds*>(smem + sizeof(LevelLds));
+    build_tree(tfb, parents + (size_t)b * N, N);
+    level_solve<uint16_t>(tfb, *reinterpret_cast<LevelLds*>(smem), mode, b, h, H, N, kD, kD, cbase,
                           cbase + VB, q, k, v, alpha, beta, S_root, o, U);
     return;
   }
-  const int Lmax = t.maxdepth + 1;
-  // gamma_n = product of alpha over anc*(n), root side first
-  if (tid < N) {
-    float g = 1.f;
-    unsigned long long m0 = t.anc[tid][0], m1 = t.anc[tid][1];
-    while (m0) {
-      const int j = __ffsll((long long)m0) - 1;
-      m0 &= m0 - 1;
-      g *= sal[j];
-    }
-    while (m1) {
-      const int j = 63 + __ffsll((long long)m1);
-      m1 &= m1 - 1;
-      g *= sal[j];
-    }
-    sga[tid] = g;
-  }
 
-  // ---- 3. ancestor-masked Gram on matrix cores ----
+  // ---- 3. ancestor-masked Gram, transposed (lane = node) ----
   {
-    const int gw = (wave + 4 - (PAIRS * 2) % 4) % 4;
+    // tile index -> (node tile nt2 in [0, 2NT): K then Q rows; ancestor tile jt <= nt2 % NT)
+    int tnt[GPW], tjt[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-      int rem = gw + 4 * i, rt = -1, jt = 0;
+      int rem = wave + 4 * i, nt2 = -1, jt = 0;
       for (int r = 0; r < 2 * NT; ++r) {
         const int cnt = (r % NT) + 1;
         if (rem >= 0 && rem < cnt) {
-          rt = r;
+          nt2 = r;
           jt = rem;
         }
         rem -= cnt;
       }
-      if (rt < 0) continue;
-      const uint16_t* X = rt < NT ? Ksh + rt * 32 * kRow : Qsh + (rt - NT) * 32 * kRow;
+      tnt[i] = nt2;
+      tjt[i] = jt;
+    }
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int nt2 = tnt[i];
+      if (nt2 < 0) continue;  // uniform
+      const bool kk = nt2 < NT;
+      const uint16_t* Xn = (kk ? Ksh : Qsh) + ((nt2 % NT) * 32 + lm) * kRow + akof;
+      const uint16_t* Kj = Ksh + (tjt[i] * 32 + lm) * kRow + akof;
       f32x16 gacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) gacc[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(X + arow * kRow + ks * 16 + akof);
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ksh + (jt * 32 + arow) * kRow + ks * 16 + akof);
-        gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kb, gacc, 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kj + ks * 16);
+        const bf16x8 bx = *reinterpret_cast<const bf16x8*>(Xn + ks * 16);
+        gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bx, gacc, 0, 0, 0);
       }
-      const bool kk = rt < NT;
-      const int col = jt * 32 + (lane & 31);
+      // keep G[j][n] when j is on n's path (j != n for K K^T), at [depth(j)][n];
+      // everything else goes to a sink slot, so the stores need no branches
+      const int n = (nt2 % NT) * 32 + lm;
+      const int nc = min(n, N - 1);
+      const unsigned long long a0 = anc_s[nc][0];
+      const unsigned long long a1 = NP > 64 ? anc_s[nc][1] : 0ull;
+      float* C = kk ? CkkD : CqkD;
+      const int Ln = __popcll(a0) + __popcll(a1);  // path length of node n
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = (rt % NT) * 32 + acc_row(r, lane);
-        if (row < N && col < N && anc_has(t, row, col)) {
-          if (kk) {
-            if (col != row) Ckk[row * kMaxL + t.depth[col]] = gacc[r];
-          } else {
-            Cqk[row * kMaxL + t.depth[col]] = gacc[r];
-          }
+        const int j = tjt[i] * 32 + acc_row(r, lane);
+        bool on;
+        int rank;
+        if constexpr (NP <= 64) {
+          on = (a0 >> j) & 1ull;
+          rank = __popcll(a0 & ((1ull << j) - 1ull));
+        } else {
+          const bool lo = j < 64;
+          const int sh = j & 63;
+          on = ((lo ? a0 : a1) >> sh) & 1ull;
+          const unsigned long long below = (1ull << sh) - 1ull;
+          rank = lo ? __popcll(a0 & below) : __popcll(a0) + __popcll(a1 & below);
         }
+        const bool keep = on && n < N && (!kk || j != n);
+        *(keep ? C + (Ln - 1 - rank) * NP + n : gsink + lane) = gacc[r];
       }
     }
   }
-  __syncthreads();
+  __syncthreads();  // path Gram entries visible
 
-  // ---- 4. per-node path solve (distance order: e_0 = n, e_1 = parent, ...) ----
-  if (tid < N) {
-    const int n = tid;
-    const int L = t.depth[n] + 1;
+  // ---- 4. path solve, one lane per node (wave 0; wave 1 too when N > 64) ----
+  // distance order: e_0 = n, e_1 = parent(n), ...; padded with zero coefficients.
+  // The trip count is the block's longest path (uniform); lanes past their own
+  // path length compute on clamped, valid addresses and keep zero outputs.
+  if (wave < SL) {
+    const int n0 = wave * 64 + lane;
+    const int n = min(n0, N - 1);
+    const unsigned long long a0 = anc_s[n][0], a1 = anc_s[n][1];
+    const int L = __popcll(a0) + __popcll(a1);
     int e[kMaxL];
-    float ea[kMaxL], eb[kMaxL];
-    unsigned long long m0 = t.anc[n][0], m1 = t.anc[n][1];
+    unsigned long long m0 = a0, m1 = a1;
 #pragma unroll
     for (int d = 0; d < kMaxL; ++d) {
       int j;
-      if (m1) {
-        j = 127 - __clzll(m1);
-        m1 &= ~(1ull << (j - 64));
-      } else if (m0) {
-        j = 63 - __clzll(m0);
-        m0 &= ~(1ull << j);
+      if constexpr (NP <= 64) {
+        j = m0 ? 63 - __clzll(m0) : n;  // past the root: zero coefficient, any valid row
+        m0 &= m0 ? ~(1ull << j) : ~0ull;
       } else {
-        j = n;  // past the root: zero coefficient, any valid row
+        if (m1) {
+          j = 127 - __clzll(m1);
+          m1 &= ~(1ull << (j - 64));
+        } else if (m0) {
+          j = 63 - __clzll(m0);
+          m0 &= ~(1ull << j);
+        } else {
+          j = n;
+        }
       }
       e[d] = j;
-      ea[d] = sal[j];
-      eb[d] = sbe[j];
     }
     float y[kMaxL], z[kMaxL];
     const int rowo = n * kMaxL;
-    const float w0 = Cqk[rowo + L - 1];
-    XW[rowo] = make_float2(1.f, w0);
-    Ep[rowo] = static_cast<uint8_t>(n);
-    y[0] = eb[0] * ea[0];
-    z[0] = w0 * eb[0] * ea[0];
-    float pi = ea[0];  // D(e_t -> n) at step t
+    const float w0 = CqkD[n];
+    float2* xwo = XWT + n;
+    if (n0 < N) xwo[0] = make_float2(1.f, w0);
+    {
+      const float a0n = sal[n], b0n = sbe[n];
+      y[0] = b0n * a0n;
+      z[0] = w0 * b0n * a0n;
+    }
+    float pi = sal[n];  // D(e_t -> n) at step t
+    // Steps go in chunks of four under one uniform branch, so that a chunk's
+    // LDS loads (all at static offsets from per-node bases) can be in flight
+    // together.  Scalar decay needs no special case: its write strengths are
+    // zero, so y = z = 0 and only the q.k term survives.  Entries past a
+    // lane's own root path are stale LDS words that only reach the
+    // discarded side of the selects.
 #pragma unroll
-    for (int tt = 1; tt < kMaxL; ++tt) {
-      float xt = 0.f, wt = 0.f;
-      if (tt < L) {  // predicated, not a break: keeps the loop fully unrolled
-        const int col = L - 1 - tt;  // depth of e_tt
-        float sx = 0.f, sw = 0.f;
-        if (gdn) {
+    for (int t0 = 1; t0 < kMaxL; t0 += 4) {
+      if (t0 < Lmax) {  // uniform
+#pragma unroll
+        for (int tt = t0; tt < t0 + 4 && tt < kMaxL; ++tt) {
+          const bool live = tt < L;
+          const float cq = CqkD[tt * NP + n];
+          const float at = sal[e[tt]];
+          const float bt = sbe[e[tt]];
+          float sx = 0.f, sw = 0.f;
 #pragma unroll
           for (int ss = 0; ss < tt; ++ss) {
-            const float gkk = Ckk[e[ss] * kMaxL + col];
+            // G(e_ss, e_tt): e_tt sits tt - ss steps above e_ss
+            const float gkk = CkkD[(tt - ss) * NP + e[ss]];
             sx = fmaf(y[ss], gkk, sx);
             sw = fmaf(z[ss], gkk, sw);
           }
+          const float xt = live ? -sx : 0.f;
+          const float wt = live ? pi * cq - sw : 0.f;
+#pragma unroll
+          for (int ss = 0; ss < tt; ++ss) {
+            y[ss] *= at;
+            z[ss] *= at;
+          }
+          y[tt] = xt * bt * at;
+          z[tt] = wt * bt * at;
+          pi *= at;
+          if (n0 < N && tt < Lmax) xwo[tt * NP] = make_float2(xt, wt);
         }
-        xt = -sx;
-        wt = pi * Cqk[rowo + col] - sw;
-        const float at = ea[tt];
-#pragma unroll
-        for (int ss = 0; ss < tt; ++ss) {
-          y[ss] *= at;
-          z[ss] *= at;
-        }
-        y[tt] = xt * eb[tt] * at;
-        z[tt] = wt * eb[tt] * at;
-        pi *= at;
-      }
-      XW[rowo + tt] = make_float2(xt, wt);
-      Ep[rowo + tt] = static_cast<uint8_t>(e[tt]);
-    }
-    Lsh[n] = L;
-  }
-
-  // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
-  bf16x8 shi[8], slo[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = sv[ks][i];
-      const __bf16 hb = static_cast<__bf16>(x);
-      shi[ks][i] = hb;
-      slo[ks][i] = static_cast<__bf16>(x - static_cast<float>(hb));
-    }
-  f32x16 kacc[PPW], qacc[PPW];
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      kacc[pi][r] = 0.f;
-      qacc[pi][r] = 0.f;
-    }
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-    for (int pi = 0; pi < PPW; ++pi) {
-      const int nt = (wave + 4 * pi) / CT;
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ksh + (nt * 32 + arow) * kRow + ks * 16 + akof);
-      const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qsh + (nt * 32 + arow) * kRow + ks * 16 + akof);
-      kacc[pi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi[ks], kb, kacc[pi], 0, 0, 0);
-      kacc[pi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo[ks], kb, kacc[pi], 0, 0, 0);
-      qacc[pi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi[ks], qb, qacc[pi], 0, 0, 0);
-      qacc[pi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo[ks], qb, qacc[pi], 0, 0, 0);
-    }
-  }
-  __syncthreads();  // K/Q staging is dead from here on: R takes its place
-
-  // ---- 6. R = beta (V - gamma KS) into LDS rows ----
-  float* Rsh = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    const int n = ((wave + 4 * pi) / CT) * 32 + arow;
-    if (n < N) {
-      const float bn = sbe[n], gn = sga[n];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 vf = bf16x4_to_f32(vv[pi][g]);
-        float4 r;
-        if (gdn) {
-          r.x = bn * (vf.x - gn * kacc[pi][4 * g + 0]);
-          r.y = bn * (vf.y - gn * kacc[pi][4 * g + 1]);
-          r.z = bn * (vf.z - gn * kacc[pi][4 * g + 2]);
-          r.w = bn * (vf.w - gn * kacc[pi][4 * g + 3]);
-        } else {
-          r = vf;
-        }
-        *reinterpret_cast<float4*>(Rsh + n * RS + col0 + 8 * g) = r;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- 7. U and o gathered over path rows of R ----
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    const int n0 = ((wave + 4 * pi) / CT) * 32 + arow;
-    const int n = min(n0, N - 1);
-    // the wave runs to its longest path; shorter paths see zero coefficients
-    int Lw = Lsh[n];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) Lw = max(Lw, __shfl_xor(Lw, m));
-    Lw = min(Lw, Lmax);
-    float4 u4[4], o4[4];
-    const float gn = sga[n];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u4[g] = f4(0.f);
-      o4[g] = make_float4(gn * qacc[pi][4 * g + 0], gn * qacc[pi][4 * g + 1],
-                          gn * qacc[pi][4 * g + 2], gn * qacc[pi][4 * g + 3]);
-    }
-    for (int tt = 0; tt < Lw; ++tt) {
-      const float2 cw = XW[n * kMaxL + tt];
-      const float* rr = Rsh + Ep[n * kMaxL + tt] * RS + col0;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 r4 = *reinterpret_cast<const float4*>(rr + 8 * g);
-        u4[g] = fma4(cw.x, r4, u4[g]);
-        o4[g] = fma4(cw.y, r4, o4[g]);
       }
     }
     if (n0 < N) {
-      float* ur = U + ((size_t)bh * N + n) * kD + cbase + col0;
-      uint16_t* orow = o + ((size_t)(b * N + n) * H + h) * kD + cbase + col0;
+      uint4 ep;
+      ep.x = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
+      ep.y = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
+      ep.z = e[8] | (e[9] << 8) | (e[10] << 16) | (e[11] << 24);
+      ep.w = e[12] | (e[13] << 8) | (e[14] << 16) | (e[15] << 24);
+      *reinterpret_cast<uint4*>(Ep + rowo) = ep;
+    }
+  }
+
+  // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
+  f32x16 kacc, qacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    kacc[r] = 0.f;
+    qacc[r] = 0.f;
+  }
+  {
+    const uint16_t* Kn = Ksh + (nt_w * 32 + lm) * kRow + akof;
+    const uint16_t* Qn = Qsh + (nt_w * 32 + lm) * kRow + akof;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 shi, slo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = sv[ks][i];
+        const __bf16 hb = static_cast<__bf16>(x);
+        shi[i] = hb;
+        slo[i] = static_cast<__bf16>(x - static_cast<float>(hb));
+      }
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kn + ks * 16);
+      const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qn + ks * 16);
+      kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, kb, kacc, 0, 0, 0);
+      kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, kb, kacc, 0, 0, 0);
+      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, qb, qacc, 0, 0, 0);
+      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, qb, qacc, 0, 0, 0);
+    }
+  }
+  __syncthreads();  // K/Q staging is dead (R takes its place); path coefficients visible
+
+  // ---- 6. R = beta (V - gamma KS) into LDS rows ----
+  float* Rsh = reinterpret_cast<float*>(smem);
+  const float my_g = sga[my_n];
+  if (my_n0 < N) {
+    const float bn = sbe[my_n];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 vf = bf16x4_to_f32(vv[g]);
+      float4 r;
+      if (gdn) {
+        r.x = bn * (vf.x - my_g * kacc[4 * g + 0]);
+        r.y = bn * (vf.y - my_g * kacc[4 * g + 1]);
+        r.z = bn * (vf.z - my_g * kacc[4 * g + 2]);
+        r.w = bn * (vf.w - my_g * kacc[4 * g + 3]);
+      } else {
+        r = vf;
+      }
+      *reinterpret_cast<float4*>(Rsh + my_n * RS + col0 + 8 * g) = r;
+    }
+  }
+  // this lane's path coefficients into registers
+  float2 xw[kMaxL];
+#pragma unroll
+  for (int tt = 0; tt < kMaxL; ++tt) xw[tt] = tt < Lmax ? XWT[tt * NP + my_n] : make_float2(0.f, 0.f);
+  const uint4 ep = *reinterpret_cast<const uint4*>(Ep + my_n * kMaxL);
+  __syncthreads();  // R rows visible
+
+  // ---- 7. U and o gathered over the node's path rows of R ----
+  // Runs to the block's longest path (shorter paths have zero coefficients);
+  // the next row's loads are issued before the current row's FMAs.
+  float4 u4[4], o4[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    u4[g] = f4(0.f);
+    o4[g] = make_float4(my_g * qacc[4 * g + 0], my_g * qacc[4 * g + 1], my_g * qacc[4 * g + 2],
+                        my_g * qacc[4 * g + 3]);
+  }
+  auto row_of = [&](int tt) {
+    const uint32_t word = tt < 4 ? ep.x : tt < 8 ? ep.y : tt < 12 ? ep.z : ep.w;
+    return Rsh + ((word >> (8 * (tt & 3))) & 0xff) * RS + col0;
+  };
+  float4 cur[4], nxt[4];
+  {
+    const float* rr = row_of(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) nxt[g] = *reinterpret_cast<const float4*>(rr + 8 * g);
+  }
+#pragma unroll
+  for (int tt = 0; tt < kMaxL; ++tt) {
+    if (tt < Lmax) {  // uniform
+#pragma unroll
+      for (int g = 0; g < 4; ++g) cur[g] = nxt[g];
+      if (tt + 1 < kMaxL && tt + 1 < Lmax) {
+        const float* rr = row_of(tt + 1 < kMaxL ? tt + 1 : tt);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) nxt[g] = *reinterpret_cast<const float4*>(rr + 8 * g);
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        *reinterpret_cast<float4*>(ur + 8 * g) = u4[g];
-        *reinterpret_cast<uint2*>(orow + 8 * g) = f32x4_to_bf16(o4[g].x, o4[g].y, o4[g].z, o4[g].w);
+        u4[g] = fma4(xw[tt].x, cur[g], u4[g]);
+        o4[g] = fma4(xw[tt].y, cur[g], o4[g]);
       }
+    }
+  }
+  if (my_n0 < N) {
+    float* ur = U + ((size_t)bh * N + my_n) * kD + cbase + col0;
+    uint16_t* orow = o + ((size_t)(b * N + my_n) * H + h) * kD + cbase + col0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      *reinterpret_cast<float4*>(ur + 8 * g) = u4[g];
+      *reinterpret_cast<uint2*>(orow + 8 * g) = f32x4_to_bf16(o4[g].x, o4[g].y, o4[g].z, o4[g].w);
     }
   }
 }
@@ -410,18 +571,14 @@ static int launch_np_vb(int B, int H, int N, int mode, const void* q, const void
 
 int launch_verify_mfma(int B, int H, int N, int mode, const void* q, const void* k, const void* v,
                        const float* alpha, const float* beta, const int32_t* parents,
-                       const float* S_root, void* o, float* U, int32_t* status, int vblock,
+                       const float* S_root, void* o, float* U, int32_t* status,
                        hipStream_t stream) {
-#define TV_MFMA_ARGS B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status, stream
-  // four waves need (node tiles x column tiles) to be a multiple of four
-  if (N <= 32) return launch_np_vb<32, 128>(TV_MFMA_ARGS);
-  if (N <= 64) {
-    if (vblock == 128) return launch_np_vb<64, 128>(TV_MFMA_ARGS);
-    return launch_np_vb<64, 64>(TV_MFMA_ARGS);
-  }
-  if (vblock == 64 || vblock == 128) return launch_np_vb<128, 64>(TV_MFMA_ARGS);
-  return launch_np_vb<128, 32>(TV_MFMA_ARGS);
-#undef TV_MFMA_ARGS
+  // node tiles x value-column tiles = 4: one output tile pair per wave
+  if (N <= 32)
+    return launch_np_vb<32, 128>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status, stream);
+  if (N <= 64)
+    return launch_np_vb<64, 64>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status, stream);
+  return launch_np_vb<128, 32>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status, stream);
 }
 
 }  // namespace tv
