@@ -139,6 +139,22 @@ def cpu_baseline(bt, max_seqs):
 
 # --------------------------------------------------------------- GPU timing
 
+def copy_calibration():
+    """A copy of known size: 256 MiB read + 256 MiB written per launch."""
+    import torch
+    nbytes = 1 << 28
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    big = torch.empty(1 << 28, device="cuda")
+    for _ in range(3):
+        big.sum()          # read-only pass over 1 GiB: evicts src and dst, leaves nothing dirty
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes,
+                                           "launches": 3}}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,7 +163,13 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device-to-device copy (three times, caches "
+                         "evicted by a read-only pass before each), to scale rocprofv3's "
+                         "FETCH_SIZE / WRITE_SIZE readings to bytes")
     a = ap.parse_args(argv)
+    if a.copy_calibration:
+        return copy_calibration()
     if a.gpus != 1:
         print(f"bench.py: --gpus {a.gpus} is not supported; this path runs on one GPU "
               "(every (sequence, head) is independent, so more GPUs only split the batch).",

@@ -27,11 +27,11 @@
 //      and, in the same pass, gamma (product of alpha over the path);
 //   3. Gram on matrix cores (32x32x16 bf16, exact products), transposed so a
 //      lane owns a node: lower-triangular blocks of K K^T and K Q^T; a lane
-//      keeps the entries whose row is on its node's path, stored by that
-//      ancestor's depth (the ancestor-masked Gram/decay builder);
-//   4. each lane solves the path of the node it will output (x for U, w for
-//      o; decays as running products of alpha, no log/exp); the coefficients
-//      stay in registers; this overlaps the S stream;
+//      keeps the entries whose row is on its node's path, stored by distance
+//      from the node (the ancestor-masked Gram/decay builder);
+//   4. one lane per node (wave 0, and wave 1 when N > 64) solves the node's
+//      path (x for U, w for o; decays as running products of alpha, no
+//      log/exp) into LDS, while the S stream is still arriving;
 //   5. Y^T = S_block^T [K;Q]^T on matrix cores with S split into bf16 hi + lo
 //      (q and k are exact in bf16: ~2^-17 relative error); the accumulator
 //      layout puts one node and 16 value columns in each lane;
