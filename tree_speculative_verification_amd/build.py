@@ -26,7 +26,7 @@ SOURCES = ["tv_api.cpp", "tv_commit.hip", "tv_verify_level.hip", "tv_verify_mfma
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-    # packed fp32 math off (see DESIGN notes): plain scalar FMAs only
+    # no packed fp32 instructions in the generated code: plain scalar FMAs only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
     f"-I{INCLUDE}", f"-I{CSRC}",

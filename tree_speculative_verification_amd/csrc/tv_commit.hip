@@ -15,9 +15,10 @@
 #include "tv_device.h"
 #include "tv_launch.h"
 
-// State rows each thread streams per tile (tile = 256 / (d_v / 4) * this rows).
-#ifndef TV_COMMIT_ROWS_PER_THREAD
-#define TV_COMMIT_ROWS_PER_THREAD 4
+// Below this many (sequence, head) states, d_v = 128 commits split each state
+// over two workgroups.
+#ifndef TV_COMMIT_SPLIT_BELOW
+#define TV_COMMIT_SPLIT_BELOW 512
 #endif
 
 namespace tv {
@@ -39,8 +40,15 @@ __global__ __launch_bounds__(kThreads) void index_kernel(int N, const int32_t* _
   if (tid == 0 && status) status[b] = bad ? 1 : 0;
 }
 
-// One workgroup per (sequence, head, tile of RT state rows).  Each thread owns
-// P float4 groups of one column group in rows r0 + rsub + p * RPP.
+// One workgroup per (sequence, head, tile of RT = RPP * P state rows); with
+// P = DV / 8 a tile is 128 rows, i.e. the whole d_k x d_v state at d_k = 128.
+// Thread t owns float4 column group t % CG of rows r0 + t / CG + p * RPP.
+//
+// Timeline of a workgroup: every state load is issued at once (after the few
+// small loads the path walk needs), the path is walked from the accepted node
+// while they are in flight, then the path's U rows and k entries are staged
+// in LDS (one dependent round trip), and the rank-len(a) update is applied in
+// registers and stored.
 template <typename TK, int DV, int P>
 __global__ __launch_bounds__(kThreads) void commit_kernel(
     int H, int N, int dk, int ntiles, const TK* __restrict__ k, const float* __restrict__ alpha,
@@ -51,13 +59,16 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   constexpr int RPP = kThreads / CG;    // rows per pass
   constexpr int RT = RPP * P;           // rows per tile
   constexpr int CH = 16;                // path entries staged per round
-  __shared__ TreeLds t;
-  __shared__ int pidx[kMaxNodes];
-  __shared__ float al[kMaxNodes];
-  __shared__ float coef[kMaxNodes];
+  constexpr int VE = 16 / sizeof(TK);   // k elements per 16-byte load
+  static_assert(RT % VE == 0, "tile rows come in whole 16-byte k chunks");
+  __shared__ int spar[kMaxNodes];
+  __shared__ float sal[kMaxNodes];
+  __shared__ int pidx[kMaxNodes];       // path, accepted node first (distance order)
+  __shared__ float coef[kMaxNodes];     // D(pidx[i] -> a): product of alpha over distances < i
   __shared__ float gam;
+  __shared__ int slen;
   __shared__ float4 ush[CH][CG];
-  __shared__ float ksh[CH][RT];
+  __shared__ __align__(16) float ksh[CH][RT];
 
   const int tid = threadIdx.x;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -69,49 +80,49 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   const int cg = tid % CG;
   const int rsub = tid / CG;
 
-  // Small loads first (parents, gates of every node, accepted index: the path
-  // is not known yet), then the state stream; loads retire in order, so the
-  // tree build waits only for the small ones.
+  // small loads first (loads retire in order), then the whole state tile
   const int pn = tid < N ? tid : N - 1;
   const int par_v = parents[(size_t)b * N + pn];
   const float a_all = alpha[(size_t)(b * N + pn) * H + h];
-  int a = accepted[b];
+  const int a_in = accepted[b];
   const float4* Sp = reinterpret_cast<const float4*>(S_root + (size_t)bh * dk * DV);
-  float4 s[P];
+  float4 acc[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int r = min(r0 + rsub + p * RPP, dk - 1);
-    s[p] = Sp[(size_t)r * CG + cg];
+    acc[p] = Sp[(size_t)r * CG + cg];
   }
-  build_tree_from(t, par_v, N);
-  if (tid < N) al[tid] = a_all;
-  const bool bad_acc = a < 0 || a >= N;
-  if (bad_acc) a = 0;
-  const int L = t.depth[a] + 1;
-  if (tid < N && anc_has(t, a, tid)) pidx[anc_rank(t, a, tid)] = tid;
-  __syncthreads();
-  if (h == 0 && tile == 0) {
-    const bool badrow = t.bad || bad_acc;
-    if (tid == 0 && status) status[b] = t.bad ? 1 : (bad_acc ? 2 : 0);
-    if (path_out && tid < N) path_out[(size_t)b * N + tid] = (!badrow && tid < L) ? pidx[tid] : -1;
+  if (tid < N) {
+    spar[tid] = par_v;
+    sal[tid] = a_all;
   }
-  // coef[i] = D(path[i] -> a): product of alpha over the path nodes after path[i]
-  if (tid < L) {
-    float c = 1.f;
-    for (int m = tid + 1; m < L; ++m) c *= al[pidx[m]];
-    coef[tid] = c;
-  }
+  const bool bad_par = __syncthreads_or(tid < N && (par_v < -1 || par_v >= tid)) != 0;
+  const bool bad_acc = a_in < 0 || a_in >= N;
   if (tid == 0) {
-    float g = 1.f;
-    for (int m = 0; m < L; ++m) g *= al[pidx[m]];
-    gam = g;
+    // walk up from the accepted node; parents[i] < i makes it end within N steps
+    int len = 0;
+    float c = 1.f;
+    if (!bad_par) {
+      for (int n = bad_acc ? 0 : a_in; n >= 0; n = spar[n]) {
+        pidx[len] = n;
+        coef[len] = c;
+        c *= sal[n];
+        ++len;
+      }
+    }
+    gam = c;
+    slen = len;
   }
   __syncthreads();
-
-  float4 acc[P];
+  const int L = slen;
+  if (h == 0 && tile == 0) {
+    if (tid == 0 && status) status[b] = bad_par ? 1 : (bad_acc ? 2 : 0);
+    if (path_out && tid < N)
+      path_out[(size_t)b * N + tid] = (!bad_par && !bad_acc && tid < L) ? pidx[L - 1 - tid] : -1;
+  }
   const float g = gam;
 #pragma unroll
-  for (int p = 0; p < P; ++p) acc[p] = mul4(g, s[p]);
+  for (int p = 0; p < P; ++p) acc[p] = mul4(g, acc[p]);
 
   const float* Ubh = U + (size_t)bh * N * DV;
   for (int j0 = 0; j0 < L; j0 += CH) {
@@ -120,12 +131,37 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
       const int jj = i / CG;
       ush[jj][i % CG] = reinterpret_cast<const float4*>(Ubh + (size_t)pidx[j0 + jj] * DV)[i % CG];
     }
-    for (int i = tid; i < nj * RT; i += kThreads) {
-      const int jj = i / RT;
-      const int r = r0 + i % RT;
+    for (int i = tid; i < nj * (RT / VE); i += kThreads) {
+      const int jj = i / (RT / VE);
+      const int rr = (i % (RT / VE)) * VE;
       const int node = pidx[j0 + jj];
-      ksh[jj][i % RT] =
-          r < dk ? coef[j0 + jj] * Elem<TK>::load(k, ((size_t)(b * N + node) * H + h) * dk + r) : 0.f;
+      const float cf = coef[j0 + jj];
+      float kv[VE];
+      if (r0 + rr < dk) {
+        const TK* kp = k + ((size_t)(b * N + node) * H + h) * dk + r0 + rr;
+        if constexpr (VE == 8) {
+          const uint4 w = *reinterpret_cast<const uint4*>(kp);
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv[2 * e] = __uint_as_float(ws[e] << 16);
+            kv[2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
+          }
+        } else {
+          const float4 w = *reinterpret_cast<const float4*>(kp);
+          kv[0] = w.x;
+          kv[1] = w.y;
+          kv[2] = w.z;
+          kv[3] = w.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) kv[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < VE; e += 4)
+        *reinterpret_cast<float4*>(&ksh[jj][rr + e]) =
+            make_float4(cf * kv[e], cf * kv[e + 1], cf * kv[e + 2], cf * kv[e + 3]);
     }
     __syncthreads();
     for (int jj = 0; jj < nj; ++jj) {
@@ -151,11 +187,11 @@ int launch_index(int B, int N, const int32_t* parents, int32_t* depth, uint64_t*
   return static_cast<int>(hipGetLastError());
 }
 
-template <typename TK, int DV>
-static int commit_dv(int B, int H, int N, int dk, const void* k, const float* alpha, const float* U,
-                     const int32_t* parents, const int32_t* accepted, const float* S_root,
-                     float* S_out, int32_t* path_out, int32_t* status, hipStream_t stream) {
-  constexpr int P = TV_COMMIT_ROWS_PER_THREAD;
+template <typename TK, int DV, int P>
+static int commit_launch(int B, int H, int N, int dk, const void* k, const float* alpha,
+                         const float* U, const int32_t* parents, const int32_t* accepted,
+                         const float* S_root, float* S_out, int32_t* path_out, int32_t* status,
+                         hipStream_t stream) {
   constexpr int RT = (kThreads / (DV / 4)) * P;
   const int ntiles = (dk + RT - 1) / RT;
   const long long nblocks = (long long)B * H * ntiles;
@@ -164,6 +200,21 @@ static int commit_dv(int B, int H, int N, int dk, const void* k, const float* al
                      H, N, dk, ntiles, static_cast<const TK*>(k), alpha, U, parents, accepted,
                      S_root, S_out, path_out, status);
   return static_cast<int>(hipGetLastError());
+}
+
+// Tiles of 128 rows (the whole state at d_k = 128); at d_v = 128 with few
+// states, 64-row tiles give twice the workgroups to spread over the CUs.
+template <typename TK, int DV>
+static int commit_dv(int B, int H, int N, int dk, const void* k, const float* alpha, const float* U,
+                     const int32_t* parents, const int32_t* accepted, const float* S_root,
+                     float* S_out, int32_t* path_out, int32_t* status, hipStream_t stream) {
+  if constexpr (DV == 128) {
+    if ((long long)B * H < TV_COMMIT_SPLIT_BELOW && dk > 64)
+      return commit_launch<TK, DV, DV / 16>(B, H, N, dk, k, alpha, U, parents, accepted, S_root,
+                                            S_out, path_out, status, stream);
+  }
+  return commit_launch<TK, DV, DV / 8>(B, H, N, dk, k, alpha, U, parents, accepted, S_root, S_out,
+                                       path_out, status, stream);
 }
 
 template <typename TK>

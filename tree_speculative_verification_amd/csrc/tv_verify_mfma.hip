@@ -50,12 +50,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kD = 128;       // d_k = d_v
 constexpr int kMaxL = 16;     // longest root-to-node path solved in registers
-constexpr int kRow = kD + 8;  // bf16 row stride of staged K/Q (16-byte pad against bank conflicts)
+// Staged K/Q rows are 256 B (16 chunks of 16 B) with chunk c of row r stored at
+// slot c ^ (r & 15): the lanes of one matrix-core operand read (consecutive
+// rows, one chunk) then hit 16 different 16-byte bank groups.
+__device__ __forceinline__ int kq_slot(int row, int ch) { return ch ^ (row & 15); }
+
+// s_waitcnt immediate: vector-memory count 0 (expcnt, lgkmcnt left alone).
+constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
 template <int NP, int VB>
 struct MfmaLayout {
   static constexpr int RS = VB + 4;                 // fp32 row stride of R in LDS
-  static constexpr int stage = 2 * NP * kRow * 2;   // K, Q bf16 until the Y contraction
+  static constexpr int stage = 2 * NP * kD * 2;     // K, Q bf16 until the Y contraction
   static constexpr int rbytes = NP * RS * 4;        // R rows, over the dead staging
   static constexpr int u0 = stage > rbytes ? stage : rbytes;
   static constexpr int fb = (int)(sizeof(LevelLds) + sizeof(TreeLds));  // level-scheduled fallback
@@ -181,7 +187,6 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   constexpr int SL = NP > 64 ? 2 : 1;         // tree nodes per lane
   constexpr int NG = NT * (NT + 1);           // lower-triangular blocks of K K^T and K Q^T
   constexpr int GPW = (NG + 3) / 4;
-  constexpr int KQPT = 2 * NP * (kD / 8) / kThreads;  // 16-byte chunks of K and Q per thread
   constexpr int RS = Lay::RS;
 
   __shared__ __align__(16) unsigned char smem[Lay::bytes];
@@ -192,15 +197,16 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   __shared__ __align__(16) float CkkD[kMaxL * NP];
   __shared__ __align__(16) float CqkD[kMaxL * NP];
   __shared__ float gsink[64];                          // Gram entries off every path land here
-  __shared__ __align__(16) float2 XWT[kMaxL * NP];     // path coefficients [distance][node] (x for U, w for o)
-  __shared__ __align__(16) uint8_t Ep[NP * kMaxL];     // path nodes [node][distance]
   __shared__ __align__(16) unsigned long long anc_s[NP][2];
+  __shared__ __align__(16) int sdep[NP];               // depth (path length - 1)
+  __shared__ __align__(16) float2 XW[kMaxL * NP];      // path coefficients [distance][node]: (x, w)
   __shared__ float sal[NP], sbe[NP], sga[NP];
   __shared__ int meta[2];                              // longest path, bad-parents flag
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int lm = lane & 31;
+  const int hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: wave-uniform branches
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int vb = bid % NVB;
@@ -211,17 +217,22 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   const bool gdn = mode == kGdn;
   const int nt_w = wave / CT;                  // this wave's node tile
   const int ct_w = wave % CT;                  // this wave's column tile
-  const int akof = 8 * (lane >> 5);
-  const int col0 = ct_w * 32 + 4 * (lane >> 5);   // + 8 g + j: this lane's columns in the block
-  const int my_n0 = nt_w * 32 + lm;            // node this lane outputs
+  const int akof = 8 * hi;
+  const int col0 = ct_w * 32 + 4 * hi;         // + 8 g + j: this lane's columns in the block
+  const int my_n0 = nt_w * 32 + lm;            // node this lane outputs (and solves for)
   const int my_n = min(my_n0, N - 1);
 
-  // ---- 1. loads: small ones first (loads retire in order) ----
+  // ---- 1-2. wave 0: gates, parents and the tree index; waves 1-3: K and Q ----
   // Row indices are clamped, not branched on: padded rows repeat row N-1 and
-  // only feed outputs that are discarded.
-  int par[SL];
-  float al[SL], be[SL];
+  // only feed outputs that are discarded.  K and Q go from HBM straight into
+  // LDS (no registers): each wave instruction fills 4 rows (1 KB) and lane i
+  // writes the 16 bytes at i * 16, so it fetches the chunk the swizzle puts
+  // there.  Wave 0 issues none of these, so nothing delays its tree build.
+  uint16_t* Ksh = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Qsh = Ksh + NP * kD;
   if (wave == 0) {
+    int par[SL];
+    float al[SL], be[SL];
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
       const int nd = min(lane + 64 * s, N - 1);
@@ -229,17 +240,55 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       al[s] = alpha[(size_t)(b * N + nd) * H + h];
       be[s] = (gdn ? beta : alpha)[(size_t)(b * N + nd) * H + h];
     }
-  }
-  uint4 kq[KQPT];
+    WaveTree<SL> T;
+    bool bad;
+    int Lmax;
+    wave_tree<SL>(T, par, al, N, bad, Lmax);
 #pragma unroll
-  for (int i = 0; i < KQPT; ++i) {
-    const int c = tid + i * kThreads;
-    const int which = c / (NP * 16);
-    const int row = min((c >> 4) % NP, N - 1);
-    const int ch = c & 15;
-    const uint16_t* src = which ? q : k;
-    kq[i] = *reinterpret_cast<const uint4*>(src + ((size_t)(b * N + row) * H + h) * kD + ch * 8);
+    for (int s = 0; s < SL; ++s) {
+      const int nd = lane + 64 * s;
+      if (nd < NP) {
+        anc_s[nd][0] = T.a0[s];
+        anc_s[nd][1] = T.a1[s];
+        sdep[nd] = __popcll(T.a0[s]) + __popcll(T.a1[s]) - 1;
+        sga[nd] = T.g[s];
+        sal[nd] = al[s];
+        sbe[nd] = gdn ? be[s] : 0.f;
+      }
+    }
+    if (lane == 0) {
+      meta[0] = Lmax;
+      meta[1] = bad;
+    }
+  } else {
+    const int slot = lane & 15;
+    for (int blk = wave - 1; blk < NP / 2; blk += 3) {  // 4-row blocks: K, then Q
+      const bool isq = blk >= NP / 4;
+      const int rb = isq ? blk - NP / 4 : blk;
+      const int row = rb * 4 + (lane >> 4);
+      const int src_row = min(row, N - 1);
+      const uint16_t* src = (isq ? q : k) + ((size_t)(b * N + src_row) * H + h) * kD +
+                            kq_slot(row, slot) * 8;
+      __builtin_amdgcn_global_load_lds(src, (isq ? Qsh : Ksh) + rb * 4 * kD, 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);  // this wave's K/Q rows have landed
   }
+  __syncthreads();  // tree, gates and K/Q staging visible
+
+  const int Lmax = __builtin_amdgcn_readfirstlane(meta[0]);  // uniform: scalar loop bounds
+  if (h == 0 && vb == 0 && tid == 0 && status) status[b] = meta[1] ? 1 : 0;
+  if (Lmax > kMaxL) {
+    __syncthreads();  // the staging area becomes the fallback's tables
+    TreeLds& tfb = *reinterpret_cast<TreeLds*>(smem + sizeof(LevelLds));
+    build_tree(tfb, parents + (size_t)b * N, N);
+    level_solve<uint16_t>(tfb, *reinterpret_cast<LevelLds*>(smem), mode, b, h, H, N, kD, kD, cbase,
+                          cbase + VB, q, k, v, alpha, beta, S_root, o, U);
+    return;
+  }
+
+  // the S columns of this wave's tile straight into MFMA operand registers, and
+  // V at the positions the outputs land on; they arrive during the Gram and
+  // the path solve
   float sv[8][8];
   {
     const float* Sb = S_root + (size_t)bh * kD * kD + cbase + ct_w * 32 + lm;
@@ -253,50 +302,6 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     const uint16_t* vr = v + ((size_t)(b * N + my_n) * H + h) * kD + cbase + col0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) vv[g] = *reinterpret_cast<const uint2*>(vr + 8 * g);
-  }
-  uint16_t* Ksh = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Qsh = Ksh + NP * kRow;
-#pragma unroll
-  for (int i = 0; i < KQPT; ++i) {
-    const int c = tid + i * kThreads;
-    const int which = c / (NP * 16);
-    const int row = (c >> 4) % NP;
-    const int ch = c & 15;
-    *reinterpret_cast<uint4*>((which ? Qsh : Ksh) + row * kRow + ch * 8) = kq[i];
-  }
-
-  // ---- 2. tree index: wave 0, in registers, then to LDS ----
-  if (wave == 0) {
-    WaveTree<SL> T;
-    bool bad;
-    int Lmax;
-    wave_tree<SL>(T, par, al, N, bad, Lmax);
-#pragma unroll
-    for (int s = 0; s < SL; ++s) {
-      const int nd = lane + 64 * s;
-      if (nd < NP) {
-        anc_s[nd][0] = T.a0[s];
-        anc_s[nd][1] = T.a1[s];
-        sga[nd] = T.g[s];
-        sal[nd] = al[s];
-        sbe[nd] = gdn ? be[s] : 0.f;
-      }
-    }
-    if (lane == 0) {
-      meta[0] = Lmax;
-      meta[1] = bad;
-    }
-  }
-  __syncthreads();  // tree, gates and K/Q staging visible
-  const int Lmax = __builtin_amdgcn_readfirstlane(meta[0]);  // uniform: scalar loop bounds
-  if (h == 0 && vb == 0 && tid == 0 && status) status[b] = meta[1] ? 1 : 0;
-  if (Lmax > kMaxL) {
-    __syncthreads();  // the staging area becomes the fallback's tables
-    TreeLds& tfb = *reinterpret_cast<TreeLds*>(smem + sizeof(LevelLds));
-    build_tree(tfb, parents + (size_t)b * N, N);
-    level_solve<uint16_t>(tfb, *reinterpret_cast<LevelLds*>(smem), mode, b, h, H, N, kD, kD, cbase,
-                          cbase + VB, q, k, v, alpha, beta, S_root, o, U);
-    return;
   }
 
   // ---- 3. ancestor-masked Gram, transposed (lane = node) ----
@@ -321,64 +326,64 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     for (int i = 0; i < GPW; ++i) {
       const int nt2 = tnt[i];
       if (nt2 < 0) continue;  // uniform
+      const int jt = tjt[i];
       const bool kk = nt2 < NT;
-      const uint16_t* Xn = (kk ? Ksh : Qsh) + ((nt2 % NT) * 32 + lm) * kRow + akof;
-      const uint16_t* Kj = Ksh + (tjt[i] * 32 + lm) * kRow + akof;
+      const uint16_t* Xn = (kk ? Ksh : Qsh) + ((nt2 % NT) * 32 + lm) * kD;
+      const uint16_t* Kj = Ksh + (jt * 32 + lm) * kD;
       f32x16 gacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) gacc[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kj + ks * 16);
-        const bf16x8 bx = *reinterpret_cast<const bf16x8*>(Xn + ks * 16);
+        const int so = kq_slot(lm, 2 * ks + hi) * 8;  // rows of a tile start at a multiple of 16
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kj + so);
+        const bf16x8 bx = *reinterpret_cast<const bf16x8*>(Xn + so);
         gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bx, gacc, 0, 0, 0);
       }
-      // keep G[j][n] when j is on n's path (j != n for K K^T), at [depth(j)][n];
-      // everything else goes to a sink slot, so the stores need no branches
-      const int n = (nt2 % NT) * 32 + lm;
+      // Keep G[j][n] when j is on n's path, at [depth(n) - depth(j)][n]; everything
+      // else goes to a sink slot, so the stores need no branches.  This lane's
+      // rows are j = 32 jt + 8 g + 4 hi + i (g, i < 4): one 32-bit word of n's
+      // ancestor set and four 16-byte reads of the depth table cover them.
+      // (The K K^T entry j = n lands at distance 0, a slot nothing reads.)
+      const int n = (nt2 % NT) * 32 + lm;  // padded lanes store to padded columns
       const int nc = min(n, N - 1);
-      const unsigned long long a0 = anc_s[nc][0];
-      const unsigned long long a1 = NP > 64 ? anc_s[nc][1] : 0ull;
-      float* C = kk ? CkkD : CqkD;
-      const int Ln = __popcll(a0) + __popcll(a1);  // path length of node n
+      const unsigned long long aw = anc_s[nc][jt >> 1];
+      const uint32_t word = static_cast<uint32_t>(aw >> (32 * (jt & 1))) >> (4 * hi);
+      const int dn = sdep[nc];
+      float* C = (kk ? CkkD : CqkD) + dn * NP + n;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = tjt[i] * 32 + acc_row(r, lane);
-        bool on;
-        int rank;
-        if constexpr (NP <= 64) {
-          on = (a0 >> j) & 1ull;
-          rank = __popcll(a0 & ((1ull << j) - 1ull));
-        } else {
-          const bool lo = j < 64;
-          const int sh = j & 63;
-          on = ((lo ? a0 : a1) >> sh) & 1ull;
-          const unsigned long long below = (1ull << sh) - 1ull;
-          rank = lo ? __popcll(a0 & below) : __popcll(a0) + __popcll(a1 & below);
+      for (int g = 0; g < 4; ++g) {
+        const int4 dj = *reinterpret_cast<const int4*>(sdep + jt * 32 + 8 * g + 4 * hi);
+        const int djs[4] = {dj.x, dj.y, dj.z, dj.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool on = (word >> (8 * g + i)) & 1u;
+          *(on ? C - djs[i] * NP : gsink + lane) = gacc[4 * g + i];
         }
-        const bool keep = on && n < N && (!kk || j != n);
-        *(keep ? C + (Ln - 1 - rank) * NP + n : gsink + lane) = gacc[r];
       }
     }
   }
   __syncthreads();  // path Gram entries visible
 
-  // ---- 4. path solve, one lane per node (wave 0; wave 1 too when N > 64) ----
-  // distance order: e_0 = n, e_1 = parent(n), ...; padded with zero coefficients.
-  // The trip count is the block's longest path (uniform); lanes past their own
-  // path length compute on clamped, valid addresses and keep zero outputs.
-  if (wave < SL) {
-    const int n0 = wave * 64 + lane;
-    const int n = min(n0, N - 1);
-    const unsigned long long a0 = anc_s[n][0], a1 = anc_s[n][1];
-    const int L = __popcll(a0) + __popcll(a1);
+  // ---- 4. path solve: lane = (node my_n, chain hi) in every wave ----
+  // Distance order e_0 = n, e_1 = parent(n), ...  Chain 0 gives x (u_n = sum_t
+  // x_t R_{e_t}), chain 1 gives w (o_n = gamma_n QS_n + sum_t w_t R_{e_t}); the
+  // two half-waves run the same code.  The trip count is the wave's longest
+  // path (uniform); lanes past their own path length compute on clamped,
+  // valid addresses and keep zero coefficients.  Scalar decay needs no special
+  // case: its write strengths are zero, so y = 0 and only the q.k term stays.
+  uint32_t ep[kMaxL / 4];  // path nodes, one byte each, distance order
+  int Lw;
+  {
     int e[kMaxL];
+    const unsigned long long a0 = anc_s[my_n][0], a1 = anc_s[my_n][1];
+    const int L = __popcll(a0) + __popcll(a1);
     unsigned long long m0 = a0, m1 = a1;
 #pragma unroll
     for (int d = 0; d < kMaxL; ++d) {
       int j;
       if constexpr (NP <= 64) {
-        j = m0 ? 63 - __clzll(m0) : n;  // past the root: zero coefficient, any valid row
+        j = m0 ? 63 - __clzll(m0) : my_n;  // past the root: zero coefficient, any valid row
         m0 &= m0 ? ~(1ull << j) : ~0ull;
       } else {
         if (m1) {
@@ -388,67 +393,53 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
           j = 63 - __clzll(m0);
           m0 &= ~(1ull << j);
         } else {
-          j = n;
+          j = my_n;
         }
       }
       e[d] = j;
     }
-    float y[kMaxL], z[kMaxL];
-    const int rowo = n * kMaxL;
-    const float w0 = CqkD[n];
-    float2* xwo = XWT + n;
-    if (n0 < N) xwo[0] = make_float2(1.f, w0);
+    int lw = L;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) lw = max(lw, __shfl_xor(lw, m));
+    Lw = __builtin_amdgcn_readfirstlane(lw);
+    const float wsel = hi ? 1.f : 0.f;
+    // this lane's chain coefficient at distance t goes to XW[t][n].x (x) or .y (w)
+    float* xwo = reinterpret_cast<float*>(XW + my_n) + hi;
+    const bool owner = my_n0 < N;
+    float y[kMaxL];
+    const float c0 = hi ? CqkD[my_n] : 1.f;
     {
-      const float a0n = sal[n], b0n = sbe[n];
-      y[0] = b0n * a0n;
-      z[0] = w0 * b0n * a0n;
+      const float a0n = sal[my_n], b0n = sbe[my_n];
+      if (owner) xwo[0] = c0;
+      y[0] = c0 * b0n * a0n;
     }
-    float pi = sal[n];  // D(e_t -> n) at step t
-    // Steps go in chunks of four under one uniform branch, so that a chunk's
-    // LDS loads (all at static offsets from per-node bases) can be in flight
-    // together.  Scalar decay needs no special case: its write strengths are
-    // zero, so y = z = 0 and only the q.k term survives.  Entries past a
-    // lane's own root path are stale LDS words that only reach the
-    // discarded side of the selects.
+    float pi = sal[my_n];  // D(e_t -> n) at step t
+    // steps in chunks of four under one uniform branch, so that a chunk's LDS
+    // loads (static offsets from per-node bases) can all be in flight together
 #pragma unroll
     for (int t0 = 1; t0 < kMaxL; t0 += 4) {
-      if (t0 < Lmax) {  // uniform
+      if (t0 < Lw) {  // uniform
 #pragma unroll
         for (int tt = t0; tt < t0 + 4 && tt < kMaxL; ++tt) {
           const bool live = tt < L;
-          const float cq = CqkD[tt * NP + n];
+          const float cq = CqkD[tt * NP + my_n];
           const float at = sal[e[tt]];
           const float bt = sbe[e[tt]];
-          float sx = 0.f, sw = 0.f;
+          float acc = 0.f;
 #pragma unroll
-          for (int ss = 0; ss < tt; ++ss) {
-            // G(e_ss, e_tt): e_tt sits tt - ss steps above e_ss
-            const float gkk = CkkD[(tt - ss) * NP + e[ss]];
-            sx = fmaf(y[ss], gkk, sx);
-            sw = fmaf(z[ss], gkk, sw);
-          }
-          const float xt = live ? -sx : 0.f;
-          const float wt = live ? pi * cq - sw : 0.f;
+          for (int ss = 0; ss < tt; ++ss) acc = fmaf(y[ss], CkkD[(tt - ss) * NP + e[ss]], acc);
+          const float c = live ? wsel * pi * cq - acc : 0.f;
 #pragma unroll
-          for (int ss = 0; ss < tt; ++ss) {
-            y[ss] *= at;
-            z[ss] *= at;
-          }
-          y[tt] = xt * bt * at;
-          z[tt] = wt * bt * at;
+          for (int ss = 0; ss < tt; ++ss) y[ss] *= at;
+          y[tt] = c * bt * at;
           pi *= at;
-          if (n0 < N && tt < Lmax) xwo[tt * NP] = make_float2(xt, wt);
+          if (owner) xwo[2 * tt * NP] = c;
         }
       }
     }
-    if (n0 < N) {
-      uint4 ep;
-      ep.x = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
-      ep.y = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
-      ep.z = e[8] | (e[9] << 8) | (e[10] << 16) | (e[11] << 24);
-      ep.w = e[12] | (e[13] << 8) | (e[14] << 16) | (e[15] << 24);
-      *reinterpret_cast<uint4*>(Ep + rowo) = ep;
-    }
+#pragma unroll
+    for (int i = 0; i < kMaxL / 4; ++i)
+      ep[i] = e[4 * i] | (e[4 * i + 1] << 8) | (e[4 * i + 2] << 16) | (e[4 * i + 3] << 24);
   }
 
   // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
@@ -459,8 +450,8 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     qacc[r] = 0.f;
   }
   {
-    const uint16_t* Kn = Ksh + (nt_w * 32 + lm) * kRow + akof;
-    const uint16_t* Qn = Qsh + (nt_w * 32 + lm) * kRow + akof;
+    const uint16_t* Kn = Ksh + (nt_w * 32 + lm) * kD;
+    const uint16_t* Qn = Qsh + (nt_w * 32 + lm) * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       bf16x8 shi, slo;
@@ -471,15 +462,16 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
         shi[i] = hb;
         slo[i] = static_cast<__bf16>(x - static_cast<float>(hb));
       }
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kn + ks * 16);
-      const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qn + ks * 16);
+      const int so = kq_slot(lm, 2 * ks + hi) * 8;
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kn + so);
+      const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qn + so);
       kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, kb, kacc, 0, 0, 0);
       kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, kb, kacc, 0, 0, 0);
       qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, qb, qacc, 0, 0, 0);
       qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, qb, qacc, 0, 0, 0);
     }
   }
-  __syncthreads();  // K/Q staging is dead (R takes its place); path coefficients visible
+  __syncthreads();  // K/Q staging is dead (R takes its place)
 
   // ---- 6. R = beta (V - gamma KS) into LDS rows ----
   float* Rsh = reinterpret_cast<float*>(smem);
@@ -501,15 +493,14 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       *reinterpret_cast<float4*>(Rsh + my_n * RS + col0 + 8 * g) = r;
     }
   }
-  // this lane's path coefficients into registers
+  // this node's path coefficients (both chains) into registers
   float2 xw[kMaxL];
 #pragma unroll
-  for (int tt = 0; tt < kMaxL; ++tt) xw[tt] = tt < Lmax ? XWT[tt * NP + my_n] : make_float2(0.f, 0.f);
-  const uint4 ep = *reinterpret_cast<const uint4*>(Ep + my_n * kMaxL);
+  for (int tt = 0; tt < kMaxL; ++tt) xw[tt] = tt < Lw ? XW[tt * NP + my_n] : make_float2(0.f, 0.f);
   __syncthreads();  // R rows visible
 
   // ---- 7. U and o gathered over the node's path rows of R ----
-  // Runs to the block's longest path (shorter paths have zero coefficients);
+  // Runs to the wave's longest path (shorter paths have zero coefficients);
   // the next row's loads are issued before the current row's FMAs.
   float4 u4[4], o4[4];
 #pragma unroll
@@ -518,10 +509,7 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     o4[g] = make_float4(my_g * qacc[4 * g + 0], my_g * qacc[4 * g + 1], my_g * qacc[4 * g + 2],
                         my_g * qacc[4 * g + 3]);
   }
-  auto row_of = [&](int tt) {
-    const uint32_t word = tt < 4 ? ep.x : tt < 8 ? ep.y : tt < 12 ? ep.z : ep.w;
-    return Rsh + ((word >> (8 * (tt & 3))) & 0xff) * RS + col0;
-  };
+  auto row_of = [&](int tt) { return Rsh + ((ep[tt >> 2] >> (8 * (tt & 3))) & 0xff) * RS + col0; };
   float4 cur[4], nxt[4];
   {
     const float* rr = row_of(0);
@@ -530,10 +518,10 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   }
 #pragma unroll
   for (int tt = 0; tt < kMaxL; ++tt) {
-    if (tt < Lmax) {  // uniform
+    if (tt < Lw) {  // uniform
 #pragma unroll
       for (int g = 0; g < 4; ++g) cur[g] = nxt[g];
-      if (tt + 1 < kMaxL && tt + 1 < Lmax) {
+      if (tt + 1 < kMaxL && tt + 1 < Lw) {
         const float* rr = row_of(tt + 1 < kMaxL ? tt + 1 : tt);
 #pragma unroll
         for (int g = 0; g < 4; ++g) nxt[g] = *reinterpret_cast<const float4*>(rr + 8 * g);
