@@ -55,6 +55,15 @@ constexpr int kMaxL = 16;     // longest root-to-node path solved in registers
 // rows, one chunk) then hit 16 different 16-byte bank groups.
 __device__ __forceinline__ int kq_slot(int row, int ch) { return ch ^ (row & 15); }
 
+// Two floats to packed bf16 (round to nearest even), first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  uint32_t r;
+  __builtin_memcpy(&r, &v, 4);
+  return r;
+}
+
 // s_waitcnt immediate: vector-memory count 0 (expcnt, lgkmcnt left alone).
 constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
@@ -372,12 +381,12 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // path (uniform); lanes past their own path length compute on clamped,
   // valid addresses and keep zero coefficients.  Scalar decay needs no special
   // case: its write strengths are zero, so y = 0 and only the q.k term stays.
-  uint32_t ep[kMaxL / 4];  // path nodes, one byte each, distance order
-  int Lw;
+  uint32_t ep[kMaxL / 4];  // path nodes, one byte each, root first (depth order)
+  int Lw, L;
   {
     int e[kMaxL];
     const unsigned long long a0 = anc_s[my_n][0], a1 = anc_s[my_n][1];
-    const int L = __popcll(a0) + __popcll(a1);
+    L = __popcll(a0) + __popcll(a1);
     unsigned long long m0 = a0, m1 = a1;
 #pragma unroll
     for (int d = 0; d < kMaxL; ++d) {
@@ -437,9 +446,33 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
         }
       }
     }
+    // depth order for the gather: ancestors have smaller indices, so the set
+    // bits of the ancestor set from the bottom up are the path root first
+    unsigned long long d0 = a0, d1 = a1;
 #pragma unroll
-    for (int i = 0; i < kMaxL / 4; ++i)
-      ep[i] = e[4 * i] | (e[4 * i + 1] << 8) | (e[4 * i + 2] << 16) | (e[4 * i + 3] << 24);
+    for (int i = 0; i < kMaxL / 4; ++i) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int j;
+        if constexpr (NP <= 64) {
+          j = d0 ? __builtin_ctzll(d0) : my_n;
+          d0 &= d0 - 1;
+        } else {
+          if (d0) {
+            j = __builtin_ctzll(d0);
+            d0 &= d0 - 1;
+          } else if (d1) {
+            j = 64 + __builtin_ctzll(d1);
+            d1 &= d1 - 1;
+          } else {
+            j = my_n;
+          }
+        }
+        w |= static_cast<uint32_t>(j) << (8 * q);
+      }
+      ep[i] = w;
+    }
   }
 
   // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
@@ -454,14 +487,18 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     const uint16_t* Qn = Qsh + (nt_w * 32 + lm) * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 shi, slo;
+      // bf16 hi and lo words, two k values per word (one packed conversion each)
+      uint32_t whi[4], wlo[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = sv[ks][i];
-        const __bf16 hb = static_cast<__bf16>(x);
-        shi[i] = hb;
-        slo[i] = static_cast<__bf16>(x - static_cast<float>(hb));
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = sv[ks][2 * i], x1 = sv[ks][2 * i + 1];
+        const uint32_t hw = pack_bf16x2(x0, x1);
+        whi[i] = hw;
+        wlo[i] = pack_bf16x2(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
       }
+      bf16x8 shi, slo;
+      __builtin_memcpy(&shi, whi, 16);
+      __builtin_memcpy(&slo, wlo, 16);
       const int so = kq_slot(lm, 2 * ks + hi) * 8;
       const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kn + so);
       const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qn + so);
@@ -493,13 +530,22 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       *reinterpret_cast<float4*>(Rsh + my_n * RS + col0 + 8 * g) = r;
     }
   }
-  // this node's path coefficients (both chains) into registers
+  // this node's path coefficients (both chains) into registers, root first:
+  // depth d is distance L - 1 - d; past the path the coefficients are zero
   float2 xw[kMaxL];
 #pragma unroll
-  for (int tt = 0; tt < kMaxL; ++tt) xw[tt] = tt < Lw ? XW[tt * NP + my_n] : make_float2(0.f, 0.f);
+  for (int tt = 0; tt < kMaxL; ++tt) {
+    if (tt < Lw) {  // uniform
+      const float2 c = XW[max(L - 1 - tt, 0) * NP + my_n];
+      xw[tt] = tt < L ? c : make_float2(0.f, 0.f);
+    } else {
+      xw[tt] = make_float2(0.f, 0.f);
+    }
+  }
   __syncthreads();  // R rows visible
 
-  // ---- 7. U and o gathered over the node's path rows of R ----
+  // ---- 7. U and o gathered over the node's path rows of R, root first ----
+  // Lanes of one subtree read the same rows near the root (LDS broadcasts).
   // Runs to the wave's longest path (shorter paths have zero coefficients);
   // the next row's loads are issued before the current row's FMAs.
   float4 u4[4], o4[4];
@@ -510,27 +556,32 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
                         my_g * qacc[4 * g + 3]);
   }
   auto row_of = [&](int tt) { return Rsh + ((ep[tt >> 2] >> (8 * (tt & 3))) & 0xff) * RS + col0; };
-  float4 cur[4], nxt[4];
-  {
-    const float* rr = row_of(0);
+  // two row buffers in turn, so the next row's loads are in flight during the
+  // current row's FMAs and no registers are copied between steps
+  auto load_row = [&](float4 (&buf)[4], int tt) {
+    const float* rr = row_of(tt);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) nxt[g] = *reinterpret_cast<const float4*>(rr + 8 * g);
-  }
+    for (int g = 0; g < 4; ++g) buf[g] = *reinterpret_cast<const float4*>(rr + 8 * g);
+  };
+  auto accum = [&](const float4 (&buf)[4], int tt) {
 #pragma unroll
-  for (int tt = 0; tt < kMaxL; ++tt) {
+    for (int g = 0; g < 4; ++g) {
+      u4[g] = fma4(xw[tt].x, buf[g], u4[g]);
+      o4[g] = fma4(xw[tt].y, buf[g], o4[g]);
+    }
+  };
+  // Steps go in pairs under one uniform branch with unconditional loads (rows
+  // past a path are valid rows with zero coefficients), which keeps each
+  // buffer in the same registers.
+  float4 ba[4], bb[4];
+  load_row(ba, 0);
+#pragma unroll
+  for (int tt = 0; tt < kMaxL; tt += 2) {
     if (tt < Lw) {  // uniform
-#pragma unroll
-      for (int g = 0; g < 4; ++g) cur[g] = nxt[g];
-      if (tt + 1 < kMaxL && tt + 1 < Lw) {
-        const float* rr = row_of(tt + 1 < kMaxL ? tt + 1 : tt);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) nxt[g] = *reinterpret_cast<const float4*>(rr + 8 * g);
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u4[g] = fma4(xw[tt].x, cur[g], u4[g]);
-        o4[g] = fma4(xw[tt].y, cur[g], o4[g]);
-      }
+      load_row(bb, tt + 1);
+      accum(ba, tt);
+      load_row(ba, tt + 2 < kMaxL ? tt + 2 : tt + 1);
+      accum(bb, tt + 1);
     }
   }
   if (my_n0 < N) {
