@@ -155,6 +155,46 @@ def copy_calibration():
     return 0
 
 
+def snapshot_baseline(tvb, sets, R, bt, stream, timed, steps, ms_tree, snap_bytes):
+    """The method the pages compare against, on the same GPU and inputs: verify by
+    walking the nodes with a full per-node state snapshot, commit by copying the
+    accepted node's snapshot.  One snapshot buffer (B H N d_k d_v floats) is shared
+    by all steps; the input sets rotate as in the main timing."""
+    import torch
+    B, N, H, dk, dv = bt.B, bt.N, bt.H, bt.dk, bt.dv
+    snaps = torch.empty((B, H, N, dk, dv), dtype=torch.float32, device=sets[0]["q"].device)
+
+    def verify(i):
+        t = sets[i % R]
+        tvb.verify_snapshot(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["parents"],
+                            t["S_root"], mode=bt.mode, snapshots=snaps, o=t["o"],
+                            status=t["st_v"], stream=stream)
+
+    def commit(i):
+        t = sets[i % R]
+        tvb.commit_snapshot(snaps, t["parents"], t["accepted"], S_out=t["S_out"],
+                            path_out=t["path"], status=t["st_c"], stream=stream)
+
+    def step(i):
+        verify(i)
+        commit(i)
+
+    k = max(3, steps // 5)
+    for i in range(2):
+        step(i)
+    ms_step, _ = timed(step, k)
+    v_ms, _ = timed(verify, k)
+    c_ms, _ = timed(commit, k)
+    del snaps
+    torch.cuda.empty_cache()
+    return {"method": "sequential per-node state snapshots (verify walks the nodes in index order "
+                      "and writes every node's full fp32 state; commit copies the accepted one)",
+            "ms_per_step": round(ms_step, 4), "nodes_per_s": round(B * N / (ms_step * 1e-3), 1),
+            "verify_us": round(v_ms * 1e3, 1), "commit_us": round(c_ms * 1e3, 1),
+            "steps": k, "snapshot_bytes": snap_bytes,
+            "speedup_tree_vs_snapshot": round(ms_step / ms_tree, 2)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +203,8 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--no-snapshot-baseline", action="store_true",
+                    help="skip timing the per-node-snapshot baseline kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (three times, caches "
                          "evicted by a read-only pass before each), to scale rocprofv3's "
@@ -242,6 +284,11 @@ def main(argv=None):
     tv_ms, _ = timed(verify, a.steps)
     tc_ms, _ = timed(commit, a.steps)
 
+    base = None
+    snap_bytes = B * H * N * dk * dv * 4
+    if not a.no_snapshot_baseline and snap_bytes <= (64 << 30):
+        base = snapshot_baseline(tvb, sets, R, bt, stream, timed, a.steps, ms_step, snap_bytes)
+
     value = B * N / (ms_step * 1e-3)
     vbytes, cbytes, L = algorithmic_bytes(bt)
     kern = {}
@@ -279,6 +326,7 @@ def main(argv=None):
                                   "ratio_snapshots_to_U": round(snap / u_only, 2),
                                   "ratio_snapshots_to_U_K_gates": round(snap / u_k_g, 2)},
         "cpu_baseline": cpu,
+        "snapshot_baseline": base,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -77,7 +77,7 @@ extern "C" {
 #define TV_ERR_DIMS (-2)     /* B, H or N <= 0, N > TV_MAX_NODES, or a size overflows */
 #define TV_ERR_HEAD_DIM (-3) /* d_k or d_v not in {16, 32, 64, 128} */
 #define TV_ERR_MODE (-4)     /* bad dtype or mode, or beta == NULL in GDN mode */
-#define TV_ERR_ALIAS (-5)    /* S_out overlaps S_root without being equal to it */
+#define TV_ERR_ALIAS (-5)    /* S_out overlaps an input it may not overlap */
 #define TV_ERR_ALGO (-6)     /* bad algo, or TV_ALGO_MFMA where it does not apply */
 #define TV_ERR_HIP_BASE (-100)
 
@@ -146,6 +146,36 @@ int tree_commit(int B, int H, int N, int dk, int dv, int dtype, const void* k, c
  */
 int tree_index(int B, int N, const int32_t* parents, int32_t* depth, uint64_t* anc,
                int32_t* status, void* stream);
+
+/*
+ * Per-node-snapshot baseline: the verification method the pages measure
+ * against (Twig abstract: existing engines verify the tree sequentially and
+ * snapshot the full state of every node; Bole abstract: recurrent layers are
+ * traversed branch by branch with a full state materialized per proposal
+ * node).  Same layer, same outputs o as tree_verify; kept for comparison on
+ * the same hardware and inputs, not as a fast path.
+ *
+ * tree_verify_snapshot -- visits the nodes of each (sequence, head) in index
+ * order, computes S_n from its parent's snapshot (S_root for parent -1) and
+ * writes it to snapshots, then o_n = S_n^T q_n.
+ *   q, k, v, alpha, beta, parents, S_root, o, status: as in tree_verify
+ *   snapshots [B, H, N, dk, dv] f32 OUT (caller-allocated: B H N dk dv 4 bytes)
+ * Bad parents are flagged in status and treated as -1.
+ */
+int tree_verify_snapshot(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta,
+                         const int32_t* parents, const float* S_root, float* snapshots, void* o,
+                         int32_t* status, void* stream);
+
+/*
+ * tree_commit_snapshot -- the baseline's commit: S_out[b, h] = snapshots[b, h,
+ * accepted[b]] (node 0 for a bad accepted index), plus path_out and status
+ * with the conventions of tree_commit.  S_out must not overlap snapshots
+ * (TV_ERR_ALIAS).
+ */
+int tree_commit_snapshot(int B, int H, int N, int dk, int dv, const float* snapshots,
+                         const int32_t* parents, const int32_t* accepted, float* S_out,
+                         int32_t* path_out, int32_t* status, void* stream);
 
 /* Text for a return code (negative) or a status code (0..2). Never NULL. */
 const char* tv_status_string(int code);

@@ -26,6 +26,8 @@ def lib():
     L.tree_verify_algo.argtypes = [I] * 7 + [P] * 10 + [I, P]
     L.tree_commit.argtypes = [I] * 6 + [P] * 10
     L.tree_index.argtypes = [I, I] + [P] * 5
+    L.tree_verify_snapshot.argtypes = [I] * 7 + [P] * 10 + [P]
+    L.tree_commit_snapshot.argtypes = [I] * 5 + [P] * 6 + [P]
     L.tv_status_string.restype = ctypes.c_char_p
     return L
 
@@ -38,7 +40,9 @@ def declared_functions():
 
 def test_header_declares_expected():
     assert declared_functions() == sorted(["tree_verify", "tree_verify_algo", "tree_commit",
-                                           "tree_index", "tv_status_string", "tv_version"])
+                                           "tree_index", "tree_verify_snapshot",
+                                           "tree_commit_snapshot", "tv_status_string",
+                                           "tv_version"])
 
 
 def test_exports_every_declared_symbol(lib):
@@ -117,6 +121,29 @@ def test_index_checks(lib):
     assert lib.tree_index(1, 4, P, None, P, None, None) == TV_ERR_NULL
     assert lib.tree_index(0, 4, P, P, P, None, None) == TV_ERR_DIMS
     assert lib.tree_index(1, 129, P, P, P, None, None) == TV_ERR_DIMS
+
+
+def test_snapshot_checks(lib):
+    P = FAKE
+    args = lambda **kw: [kw.get("B", 1), kw.get("H", 1), kw.get("N", 4), kw.get("dk", 16),
+                         kw.get("dv", 16), kw.get("dtype", 0), kw.get("mode", 0)]
+    ptrs = [P] * 9 + [None]   # q k v alpha beta parents S_root snapshots o, status = NULL
+    assert lib.tree_verify_snapshot(*args(), *([None] + ptrs[1:]), None) == TV_ERR_NULL
+    assert lib.tree_verify_snapshot(*args(), *(ptrs[:7] + [None] + ptrs[8:]), None) == TV_ERR_NULL
+    assert lib.tree_verify_snapshot(*args(N=129), *ptrs, None) == TV_ERR_DIMS
+    assert lib.tree_verify_snapshot(*args(dv=48), *ptrs, None) == TV_ERR_HEAD_DIM
+    assert lib.tree_verify_snapshot(*args(mode=3), *ptrs, None) == TV_ERR_MODE
+    nob = ptrs[:4] + [None] + ptrs[5:]
+    assert lib.tree_verify_snapshot(*args(), *nob, None) == TV_ERR_MODE   # GDN needs beta
+    # B H N d_k d_v beyond 2^44 floats of snapshots
+    assert lib.tree_verify_snapshot(*args(B=1 << 20, H=64, N=128, dk=128, dv=128), *ptrs, None) == TV_ERR_DIMS
+    assert lib.tree_commit_snapshot(1, 1, 4, 16, 16, None, P, P, P, None, None, None) == TV_ERR_NULL
+    assert lib.tree_commit_snapshot(1, 1, 4, 16, 16, P, P, None, P, None, None, None) == TV_ERR_NULL
+    assert lib.tree_commit_snapshot(1, 1, 0, 16, 16, P, P, P, P, None, None, None) == TV_ERR_DIMS
+    # S_out inside the snapshot buffer
+    s0 = ctypes.c_void_p(0x100000)
+    s1 = ctypes.c_void_p(0x100000 + 4 * 16 * 16)
+    assert lib.tree_commit_snapshot(1, 1, 4, 16, 16, s0, P, P, s1, None, None, None) == TV_ERR_ALIAS
 
 
 def test_product_path_has_no_oracle_import():

@@ -20,8 +20,8 @@ TV_GDN, TV_SCALAR_DECAY = 0, 1
 TV_ALGO_AUTO, TV_ALGO_LEVEL, TV_ALGO_MFMA = 0, 1, 2
 TV_MAX_NODES = 128
 
-SYMBOLS = ["tree_verify", "tree_verify_algo", "tree_commit", "tree_index", "tv_status_string",
-           "tv_version"]
+SYMBOLS = ["tree_verify", "tree_verify_algo", "tree_commit", "tree_index", "tree_verify_snapshot",
+           "tree_commit_snapshot", "tv_status_string", "tv_version"]
 
 
 class TreeVerifyError(RuntimeError):
@@ -44,6 +44,10 @@ def _load() -> ctypes.CDLL:
     lib.tree_commit.restype = I
     lib.tree_index.argtypes = [I, I, P, P, P, P, P]
     lib.tree_index.restype = I
+    lib.tree_verify_snapshot.argtypes = [I] * 7 + [P] * 10 + [P]
+    lib.tree_verify_snapshot.restype = I
+    lib.tree_commit_snapshot.argtypes = [I] * 5 + [P] * 6 + [P]
+    lib.tree_commit_snapshot.restype = I
     lib.tv_status_string.argtypes = [I]
     lib.tv_status_string.restype = ctypes.c_char_p
     lib.tv_version.argtypes = []
@@ -163,3 +167,59 @@ def index(parents, stream=None):
     if rc != 0:
         raise TreeVerifyError(rc, "tree_index")
     return depth, anc, status
+
+
+def verify_snapshot(q, k, v, alpha, beta, parents, S_root, mode=TV_GDN, snapshots=None, o=None,
+                    status=None, stream=None):
+    """Per-node-snapshot baseline: o [B,N,H,dv], snapshots [B,H,N,dk,dv] f32, status [B]."""
+    B, N, H, dk = q.shape
+    dv = v.shape[3]
+    dev = q.device
+    dt = q.dtype
+    _check(q, "q", (B, N, H, dk), dt, dev)
+    _check(k, "k", (B, N, H, dk), dt, dev)
+    _check(v, "v", (B, N, H, dv), dt, dev)
+    _check(alpha, "alpha", (B, N, H), torch.float32, dev)
+    if mode == TV_GDN or beta is not None:
+        _check(beta, "beta", (B, N, H), torch.float32, dev)
+    _check(parents, "parents", (B, N), torch.int32, dev)
+    _check(S_root, "S_root", (B, H, dk, dv), torch.float32, dev)
+    if snapshots is None:
+        snapshots = torch.empty((B, H, N, dk, dv), dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty((B, N, H, dv), dtype=dt, device=dev)
+    if status is None:
+        status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(snapshots, "snapshots", (B, H, N, dk, dv), torch.float32, dev)
+    _check(o, "o", (B, N, H, dv), dt, dev)
+    _check(status, "status", (B,), torch.int32, dev)
+    rc = LIB.tree_verify_snapshot(B, H, N, dk, dv, _dtype_code(q), mode, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(alpha), _ptr(beta), _ptr(parents), _ptr(S_root),
+                                  _ptr(snapshots), _ptr(o), _ptr(status), _stream(stream))
+    if rc != 0:
+        raise TreeVerifyError(rc, "tree_verify_snapshot")
+    return o, snapshots, status
+
+
+def commit_snapshot(snapshots, parents, accepted, S_out=None, path_out=None, status=None,
+                    stream=None):
+    """The baseline's commit: S_out [B,H,dk,dv] = the accepted node's snapshot; path, status."""
+    B, H, N, dk, dv = snapshots.shape
+    dev = snapshots.device
+    _check(snapshots, "snapshots", (B, H, N, dk, dv), torch.float32, dev)
+    _check(parents, "parents", (B, N), torch.int32, dev)
+    _check(accepted, "accepted", (B,), torch.int32, dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if path_out is None:
+        path_out = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(S_out, "S_out", (B, H, dk, dv), torch.float32, dev)
+    _check(path_out, "path_out", (B, N), torch.int32, dev)
+    _check(status, "status", (B,), torch.int32, dev)
+    rc = LIB.tree_commit_snapshot(B, H, N, dk, dv, _ptr(snapshots), _ptr(parents), _ptr(accepted),
+                                  _ptr(S_out), _ptr(path_out), _ptr(status), _stream(stream))
+    if rc != 0:
+        raise TreeVerifyError(rc, "tree_commit_snapshot")
+    return S_out, path_out, status

@@ -22,7 +22,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtreeverify.so")
 ARCH = "gfx950"
 
-SOURCES = ["tv_api.cpp", "tv_commit.hip", "tv_verify_level.hip", "tv_verify_mfma.hip"]
+SOURCES = ["tv_api.cpp", "tv_commit.hip", "tv_verify_level.hip", "tv_verify_mfma.hip",
+           "tv_snapshot.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -18,6 +18,12 @@ bool sizes_ok(long long B, long long H, long long N, long long dk, long long dv)
          B * H <= big / (dk * dv);
 }
 
+// The snapshot buffer (B H N d_k d_v floats) stays below 2^46 bytes.
+bool snapshot_size_ok(long long B, long long H, long long N, long long dk, long long dv) {
+  const long long big = 1LL << 44;
+  return B * H <= big / N && B * H * N <= big / (dk * dv);
+}
+
 int hip_code(int err) { return err == 0 ? TV_OK : TV_ERR_HIP_BASE - err; }
 
 int check_common(int B, int H, int N, int dk, int dv, int dtype) {
@@ -85,6 +91,37 @@ int tree_index(int B, int N, const int32_t* parents, int32_t* depth, uint64_t* a
   return hip_code(tv::launch_index(B, N, parents, depth, anc, status, static_cast<hipStream_t>(stream)));
 }
 
+int tree_verify_snapshot(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta,
+                         const int32_t* parents, const float* S_root, float* snapshots, void* o,
+                         int32_t* status, void* stream) {
+  if (!q || !k || !v || !alpha || !parents || !S_root || !snapshots || !o) return TV_ERR_NULL;
+  int rc = check_common(B, H, N, dk, dv, dtype);
+  if (rc) return rc;
+  if (mode != TV_GDN && mode != TV_SCALAR_DECAY) return TV_ERR_MODE;
+  if (mode == TV_GDN && !beta) return TV_ERR_MODE;
+  if (!snapshot_size_ok(B, H, N, dk, dv)) return TV_ERR_DIMS;
+  return hip_code(tv::launch_snapshot_verify(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta,
+                                             parents, S_root, snapshots, o, status,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int tree_commit_snapshot(int B, int H, int N, int dk, int dv, const float* snapshots,
+                         const int32_t* parents, const int32_t* accepted, float* S_out,
+                         int32_t* path_out, int32_t* status, void* stream) {
+  if (!snapshots || !parents || !accepted || !S_out) return TV_ERR_NULL;
+  int rc = check_common(B, H, N, dk, dv, TV_F32);
+  if (rc) return rc;
+  if (!snapshot_size_ok(B, H, N, dk, dv)) return TV_ERR_DIMS;
+  const uintptr_t sb = reinterpret_cast<uintptr_t>(snapshots);
+  const uintptr_t se = sb + (uintptr_t)B * H * N * dk * dv * sizeof(float);
+  const uintptr_t ob = reinterpret_cast<uintptr_t>(S_out);
+  const uintptr_t oe = ob + (uintptr_t)B * H * dk * dv * sizeof(float);
+  if (ob < se && sb < oe) return TV_ERR_ALIAS;
+  return hip_code(tv::launch_snapshot_commit(B, H, N, dk, dv, snapshots, parents, accepted, S_out,
+                                             path_out, status, static_cast<hipStream_t>(stream)));
+}
+
 const char* tv_status_string(int code) {
   switch (code) {
     case TV_OK: return "ok";
@@ -94,7 +131,7 @@ const char* tv_status_string(int code) {
     case TV_ERR_DIMS: return "bad sizes: B, H, N must be positive, N <= 128, sizes must fit";
     case TV_ERR_HEAD_DIM: return "d_k and d_v must be 16, 32, 64 or 128";
     case TV_ERR_MODE: return "bad dtype or mode, or beta is NULL in gated-delta-rule mode";
-    case TV_ERR_ALIAS: return "S_out overlaps S_root without being the same buffer";
+    case TV_ERR_ALIAS: return "S_out overlaps an input buffer (other than S_out == S_root in tree_commit)";
     case TV_ERR_ALGO: return "bad solver choice for these arguments";
   }
   if (code <= TV_ERR_HIP_BASE) return "HIP launch failed (code = -(100 + hipError_t))";

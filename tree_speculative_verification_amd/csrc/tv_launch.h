@@ -26,4 +26,13 @@ int launch_verify_mfma(int B, int H, int N, int mode, const void* q, const void*
                        const float* S_root, void* o, float* U, int32_t* status,
                        hipStream_t stream);
 
+// Per-node-snapshot baseline (tv_snapshot.hip).
+int launch_snapshot_verify(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                           const void* k, const void* v, const float* alpha, const float* beta,
+                           const int32_t* parents, const float* S_root, float* snap, void* o,
+                           int32_t* status, hipStream_t stream);
+int launch_snapshot_commit(int B, int H, int N, int dk, int dv, const float* snap,
+                           const int32_t* parents, const int32_t* accepted, float* S_out,
+                           int32_t* path_out, int32_t* status, hipStream_t stream);
+
 }  // namespace tv
