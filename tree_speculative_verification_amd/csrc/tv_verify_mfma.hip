@@ -411,18 +411,21 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) lw = max(lw, __shfl_xor(lw, m));
     Lw = __builtin_amdgcn_readfirstlane(lw);
+    // The decay between path nodes factors through the running product
+    // Q_t = D(e_t -> n) = alpha(e_0) ... alpha(e_{t-1}):  D(e_t -> e_s) = Q_t / Q_s.
+    // So with c_t = Q_t h_t the substitution runs on decay-free h:
+    //   h_t = w_sel (q_n . k_{e_t}) - sum_{s<t} beta(e_s) h_s G(e_s, e_t)
+    // (h_0 = 1 for x), one FMA per pair and no rescaling; Q_t only scales the
+    // coefficient written out.
     const float wsel = hi ? 1.f : 0.f;
     // this lane's chain coefficient at distance t goes to XW[t][n].x (x) or .y (w)
     float* xwo = reinterpret_cast<float*>(XW + my_n) + hi;
     const bool owner = my_n0 < N;
-    float y[kMaxL];
+    float y[kMaxL];  // beta(e_s) h_s
     const float c0 = hi ? CqkD[my_n] : 1.f;
-    {
-      const float a0n = sal[my_n], b0n = sbe[my_n];
-      if (owner) xwo[0] = c0;
-      y[0] = c0 * b0n * a0n;
-    }
-    float pi = sal[my_n];  // D(e_t -> n) at step t
+    if (owner) xwo[0] = c0;
+    y[0] = c0 * sbe[my_n];
+    float qt = sal[my_n];  // Q_t at step t
     // steps in chunks of four under one uniform branch, so that a chunk's LDS
     // loads (static offsets from per-node bases) can all be in flight together
 #pragma unroll
@@ -434,15 +437,13 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
           const float cq = CqkD[tt * NP + my_n];
           const float at = sal[e[tt]];
           const float bt = sbe[e[tt]];
-          float acc = 0.f;
+          float acc = wsel * cq;
 #pragma unroll
-          for (int ss = 0; ss < tt; ++ss) acc = fmaf(y[ss], CkkD[(tt - ss) * NP + e[ss]], acc);
-          const float c = live ? wsel * pi * cq - acc : 0.f;
-#pragma unroll
-          for (int ss = 0; ss < tt; ++ss) y[ss] *= at;
-          y[tt] = c * bt * at;
-          pi *= at;
-          if (owner) xwo[2 * tt * NP] = c;
+          for (int ss = 0; ss < tt; ++ss) acc = fmaf(-y[ss], CkkD[(tt - ss) * NP + e[ss]], acc);
+          const float hv = live ? acc : 0.f;
+          y[tt] = hv * bt;
+          if (owner) xwo[2 * tt * NP] = qt * hv;
+          qt *= at;
         }
       }
     }
@@ -494,7 +495,10 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
         const float x0 = sv[ks][2 * i], x1 = sv[ks][2 * i + 1];
         const uint32_t hw = pack_bf16x2(x0, x1);
         whi[i] = hw;
-        wlo[i] = pack_bf16x2(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
+        // hi value of x0 back as a float: its 16 bits moved up by a byte permute
+        // (a shift here gets rewritten as a second conversion of x0)
+        const float h0 = __uint_as_float(__builtin_amdgcn_perm(0u, hw, 0x01000c0cu));
+        wlo[i] = pack_bf16x2(x0 - h0, x1 - __uint_as_float(hw & 0xffff0000u));
       }
       bf16x8 shi, slo;
       __builtin_memcpy(&shi, whi, 16);
