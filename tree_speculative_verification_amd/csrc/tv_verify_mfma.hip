@@ -224,8 +224,14 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   const int b = bh / H;
   const int cbase = vb * VB;
   const bool gdn = mode == kGdn;
-  const int nt_w = wave / CT;                  // this wave's node tile
-  const int ct_w = wave % CT;                  // this wave's column tile
+  // With two node tiles (KS = 2) the two waves of a column tile split the d_k
+  // contraction instead of each streaming the whole S block: wave (kh, ct)
+  // loads rows 64 kh .. 64 kh + 63 and forms partial products for both node
+  // tiles; the halves meet in LDS after the contraction (step 5).  It then
+  // owns node tile kh for steps 4, 6 and 7.
+  constexpr int KS = NT == 2 ? 2 : 1;          // d_k split of the S contraction
+  const int nt_w = KS == 2 ? (wave & 1) : wave / CT;    // this wave's node tile
+  const int ct_w = KS == 2 ? (wave >> 1) : wave % CT;   // this wave's column tile
   const int akof = 8 * hi;
   const int col0 = ct_w * 32 + 4 * hi;         // + 8 g + j: this lane's columns in the block
   const int my_n0 = nt_w * 32 + lm;            // node this lane outputs (and solves for)
@@ -298,11 +304,13 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // the S columns of this wave's tile straight into MFMA operand registers, and
   // V at the positions the outputs land on; they arrive during the Gram and
   // the path solve
-  float sv[8][8];
+  constexpr int KSTEPS = 8 / KS;                // 16-row k steps of this wave
+  float sv[KSTEPS][8];
   {
-    const float* Sb = S_root + (size_t)bh * kD * kD + cbase + ct_w * 32 + lm;
+    const float* Sb = S_root + (size_t)bh * kD * kD + cbase + ct_w * 32 + lm +
+                      (size_t)(KS == 2 ? nt_w * 64 : 0) * kD;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int i = 0; i < 8; ++i) sv[ks][i] = Sb[(size_t)(ks * 16 + akof + i) * kD];
   }
@@ -477,32 +485,36 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   }
 
   // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
+  // S is split into bf16 hi and lo words, two k values per word (one packed
+  // conversion each); q and k are exact in bf16.
+  auto split = [&](int ks, bf16x8& shi, bf16x8& slo) {
+    uint32_t whi[4], wlo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = sv[ks][2 * i], x1 = sv[ks][2 * i + 1];
+      const uint32_t hw = pack_bf16x2(x0, x1);
+      whi[i] = hw;
+      // hi value of x0 back as a float: its 16 bits moved up by a byte permute
+      // (a shift here gets rewritten as a second conversion of x0)
+      const float h0 = __uint_as_float(__builtin_amdgcn_perm(0u, hw, 0x01000c0cu));
+      wlo[i] = pack_bf16x2(x0 - h0, x1 - __uint_as_float(hw & 0xffff0000u));
+    }
+    __builtin_memcpy(&shi, whi, 16);
+    __builtin_memcpy(&slo, wlo, 16);
+  };
   f32x16 kacc, qacc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     kacc[r] = 0.f;
     qacc[r] = 0.f;
   }
-  {
+  if constexpr (KS == 1) {
     const uint16_t* Kn = Ksh + (nt_w * 32 + lm) * kD;
     const uint16_t* Qn = Qsh + (nt_w * 32 + lm) * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      // bf16 hi and lo words, two k values per word (one packed conversion each)
-      uint32_t whi[4], wlo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = sv[ks][2 * i], x1 = sv[ks][2 * i + 1];
-        const uint32_t hw = pack_bf16x2(x0, x1);
-        whi[i] = hw;
-        // hi value of x0 back as a float: its 16 bits moved up by a byte permute
-        // (a shift here gets rewritten as a second conversion of x0)
-        const float h0 = __uint_as_float(__builtin_amdgcn_perm(0u, hw, 0x01000c0cu));
-        wlo[i] = pack_bf16x2(x0 - h0, x1 - __uint_as_float(hw & 0xffff0000u));
-      }
       bf16x8 shi, slo;
-      __builtin_memcpy(&shi, whi, 16);
-      __builtin_memcpy(&slo, wlo, 16);
+      split(ks, shi, slo);
       const int so = kq_slot(lm, 2 * ks + hi) * 8;
       const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kn + so);
       const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qn + so);
@@ -511,8 +523,63 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, qb, qacc, 0, 0, 0);
       qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, qb, qacc, 0, 0, 0);
     }
+    __syncthreads();  // K/Q staging is dead (R takes its place)
+  } else {
+    // partial products over this wave's half of d_k, for both node tiles: the
+    // own tile (nt_w) accumulates in kacc/qacc, the other in kx/qx
+    f32x16 kx, qx;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      kx[r] = 0.f;
+      qx[r] = 0.f;
+    }
+    const uint16_t* Kn = Ksh + (nt_w * 32 + lm) * kD;
+    const uint16_t* Qn = Qsh + (nt_w * 32 + lm) * kD;
+    const uint16_t* Ko = Ksh + ((1 - nt_w) * 32 + lm) * kD;
+    const uint16_t* Qo = Qsh + ((1 - nt_w) * 32 + lm) * kD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 shi, slo;
+      split(ks, shi, slo);
+      const int so = kq_slot(lm, nt_w * 8 + 2 * ks + hi) * 8;
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kn + so);
+      const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qn + so);
+      const bf16x8 kob = *reinterpret_cast<const bf16x8*>(Ko + so);
+      const bf16x8 qob = *reinterpret_cast<const bf16x8*>(Qo + so);
+      kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, kb, kacc, 0, 0, 0);
+      kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, kb, kacc, 0, 0, 0);
+      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, qb, qacc, 0, 0, 0);
+      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, qb, qacc, 0, 0, 0);
+      kx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, kob, kx, 0, 0, 0);
+      kx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, kob, kx, 0, 0, 0);
+      qx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, qob, qx, 0, 0, 0);
+      qx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, qob, qx, 0, 0, 0);
+    }
+    __syncthreads();  // K/Q staging is dead: it carries the partial products now
+    // wave w hands its partial for the partner's tile to the partner (w ^ 1),
+    // as float4 groups [wave][group][lane] (consecutive lanes, no conflicts)
+    float4* xo = reinterpret_cast<float4*>(smem) + wave * (8 * 64) + lane;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      xo[g * 64] = make_float4(kx[4 * g], kx[4 * g + 1], kx[4 * g + 2], kx[4 * g + 3]);
+      xo[(4 + g) * 64] = make_float4(qx[4 * g], qx[4 * g + 1], qx[4 * g + 2], qx[4 * g + 3]);
+    }
+    __syncthreads();  // partials visible
+    const float4* xi = reinterpret_cast<const float4*>(smem) + (wave ^ 1) * (8 * 64) + lane;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 pk = xi[g * 64], pq = xi[(4 + g) * 64];
+      kacc[4 * g] += pk.x;
+      kacc[4 * g + 1] += pk.y;
+      kacc[4 * g + 2] += pk.z;
+      kacc[4 * g + 3] += pk.w;
+      qacc[4 * g] += pq.x;
+      qacc[4 * g + 1] += pq.y;
+      qacc[4 * g + 2] += pq.z;
+      qacc[4 * g + 3] += pq.w;
+    }
+    __syncthreads();  // partials consumed (R takes their place)
   }
-  __syncthreads();  // K/Q staging is dead (R takes its place)
 
   // ---- 6. R = beta (V - gamma KS) into LDS rows ----
   float* Rsh = reinterpret_cast<float*>(smem);
