@@ -210,7 +210,10 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   __shared__ __align__(16) int sdep[NP];               // depth (path length - 1)
   __shared__ __align__(16) float2 XW[kMaxL * NP];      // path coefficients [distance][node]: (x, w)
   __shared__ float sal[NP], sbe[NP], sga[NP];
-  __shared__ int meta[2];                              // longest path, bad-parents flag
+  __shared__ int meta[2 + NT];                         // longest path, bad-parents flag, longest per node tile
+  // each node's root path, one byte per node, in distance order (n, parent,
+  // ...), padded with the node itself
+  __shared__ __align__(16) uint4 sEd[NP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -262,14 +265,48 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
       const int nd = lane + 64 * s;
+      const int Ln = __popcll(T.a0[s]) + __popcll(T.a1[s]);
       if (nd < NP) {
         anc_s[nd][0] = T.a0[s];
         anc_s[nd][1] = T.a1[s];
-        sdep[nd] = __popcll(T.a0[s]) + __popcll(T.a1[s]) - 1;
+        sdep[nd] = Ln - 1;
         sga[nd] = T.g[s];
         sal[nd] = al[s];
         sbe[nd] = gdn ? be[s] : 0.f;
+        // Path list in distance order (n, parent, ...), padded with n, computed
+        // here while K and Q are still in flight: ancestors have smaller
+        // indices, so it is the ancestor set's bits from the top.  Steps past
+        // the tree's longest path (uniform) only pad.
+        uint32_t wd[kMaxL / 4] = {0u, 0u, 0u, 0u};
+        unsigned long long h0 = T.a0[s], h1 = T.a1[s];
+#pragma unroll
+        for (int d = 0; d < kMaxL; ++d) {
+          int jd = nd;
+          if (d < Lmax) {  // uniform
+            if constexpr (NP <= 64) {
+              if (h0) {
+                jd = 63 - __clzll(h0);
+                h0 ^= 1ull << jd;
+              }
+            } else {
+              if (h1) {
+                jd = 127 - __clzll(h1);
+                h1 ^= 1ull << (jd - 64);
+              } else if (h0) {
+                jd = 63 - __clzll(h0);
+                h0 ^= 1ull << jd;
+              }
+            }
+          }
+          wd[d >> 2] |= static_cast<uint32_t>(jd) << (8 * (d & 3));
+        }
+        sEd[nd] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
       }
+      // longest path per node tile of 32 (the lane halves of this slot)
+      int lt = nd < N ? Ln : 1;
+#pragma unroll
+      for (int m = 16; m >= 1; m >>= 1) lt = max(lt, __shfl_xor(lt, m));
+      if ((lane & 31) == 0 && 2 * s + (lane >> 5) < NT) meta[2 + 2 * s + (lane >> 5)] = lt;
     }
     if (lane == 0) {
       meta[0] = Lmax;
@@ -389,36 +426,18 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // path (uniform); lanes past their own path length compute on clamped,
   // valid addresses and keep zero coefficients.  Scalar decay needs no special
   // case: its write strengths are zero, so y = 0 and only the q.k term stays.
-  uint32_t ep[kMaxL / 4];  // path nodes, one byte each, root first (depth order)
+  uint4 ep;  // path nodes, one byte each, distance order, for the gather
   int Lw, L;
   {
     int e[kMaxL];
-    const unsigned long long a0 = anc_s[my_n][0], a1 = anc_s[my_n][1];
-    L = __popcll(a0) + __popcll(a1);
-    unsigned long long m0 = a0, m1 = a1;
+    L = sdep[my_n] + 1;
+    {
+      const uint4 ed = sEd[my_n];
+      const uint32_t w4[4] = {ed.x, ed.y, ed.z, ed.w};
 #pragma unroll
-    for (int d = 0; d < kMaxL; ++d) {
-      int j;
-      if constexpr (NP <= 64) {
-        j = m0 ? 63 - __clzll(m0) : my_n;  // past the root: zero coefficient, any valid row
-        m0 &= m0 ? ~(1ull << j) : ~0ull;
-      } else {
-        if (m1) {
-          j = 127 - __clzll(m1);
-          m1 &= ~(1ull << (j - 64));
-        } else if (m0) {
-          j = 63 - __clzll(m0);
-          m0 &= ~(1ull << j);
-        } else {
-          j = my_n;
-        }
-      }
-      e[d] = j;
+      for (int d = 0; d < kMaxL; ++d) e[d] = (w4[d >> 2] >> (8 * (d & 3))) & 0xff;
     }
-    int lw = L;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) lw = max(lw, __shfl_xor(lw, m));
-    Lw = __builtin_amdgcn_readfirstlane(lw);
+    Lw = __builtin_amdgcn_readfirstlane(meta[2 + nt_w]);  // this wave's longest path
     // The decay between path nodes factors through the running product
     // Q_t = D(e_t -> n) = alpha(e_0) ... alpha(e_{t-1}):  D(e_t -> e_s) = Q_t / Q_s.
     // So with c_t = Q_t h_t the substitution runs on decay-free h:
@@ -434,13 +453,15 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     if (owner) xwo[0] = c0;
     y[0] = c0 * sbe[my_n];
     float qt = sal[my_n];  // Q_t at step t
-    // steps in chunks of four under one uniform branch, so that a chunk's LDS
-    // loads (static offsets from per-node bases) can all be in flight together
+    // steps in chunks under one uniform branch, so that a chunk's LDS loads
+    // (static offsets from per-node bases) can all be in flight together; the
+    // chunk is shorter when the whole S block is held in registers (KS = 1)
+    constexpr int CHK = KS == 2 ? 4 : 2;
 #pragma unroll
-    for (int t0 = 1; t0 < kMaxL; t0 += 4) {
+    for (int t0 = 1; t0 < kMaxL; t0 += CHK) {
       if (t0 < Lw) {  // uniform
 #pragma unroll
-        for (int tt = t0; tt < t0 + 4 && tt < kMaxL; ++tt) {
+        for (int tt = t0; tt < t0 + CHK && tt < kMaxL; ++tt) {
           const bool live = tt < L;
           const float cq = CqkD[tt * NP + my_n];
           const float at = sal[e[tt]];
@@ -455,33 +476,10 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
         }
       }
     }
-    // depth order for the gather: ancestors have smaller indices, so the set
-    // bits of the ancestor set from the bottom up are the path root first
-    unsigned long long d0 = a0, d1 = a1;
-#pragma unroll
-    for (int i = 0; i < kMaxL / 4; ++i) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int j;
-        if constexpr (NP <= 64) {
-          j = d0 ? __builtin_ctzll(d0) : my_n;
-          d0 &= d0 - 1;
-        } else {
-          if (d0) {
-            j = __builtin_ctzll(d0);
-            d0 &= d0 - 1;
-          } else if (d1) {
-            j = 64 + __builtin_ctzll(d1);
-            d1 &= d1 - 1;
-          } else {
-            j = my_n;
-          }
-        }
-        w |= static_cast<uint32_t>(j) << (8 * q);
-      }
-      ep[i] = w;
-    }
+    ep = make_uint4(e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24),
+                    e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24),
+                    e[8] | (e[9] << 8) | (e[10] << 16) | (e[11] << 24),
+                    e[12] | (e[13] << 8) | (e[14] << 16) | (e[15] << 24));
   }
 
   // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
@@ -601,22 +599,13 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       *reinterpret_cast<float4*>(Rsh + my_n * RS + col0 + 8 * g) = r;
     }
   }
-  // this node's path coefficients (both chains) into registers, root first:
-  // depth d is distance L - 1 - d; past the path the coefficients are zero
+  // this node's path coefficients (both chains) into registers
   float2 xw[kMaxL];
 #pragma unroll
-  for (int tt = 0; tt < kMaxL; ++tt) {
-    if (tt < Lw) {  // uniform
-      const float2 c = XW[max(L - 1 - tt, 0) * NP + my_n];
-      xw[tt] = tt < L ? c : make_float2(0.f, 0.f);
-    } else {
-      xw[tt] = make_float2(0.f, 0.f);
-    }
-  }
+  for (int tt = 0; tt < kMaxL; ++tt) xw[tt] = tt < Lw ? XW[tt * NP + my_n] : make_float2(0.f, 0.f);
   __syncthreads();  // R rows visible
 
-  // ---- 7. U and o gathered over the node's path rows of R, root first ----
-  // Lanes of one subtree read the same rows near the root (LDS broadcasts).
+  // ---- 7. U and o gathered over the node's path rows of R ----
   // Runs to the wave's longest path (shorter paths have zero coefficients);
   // the next row's loads are issued before the current row's FMAs.
   float4 u4[4], o4[4];
@@ -626,7 +615,8 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     o4[g] = make_float4(my_g * qacc[4 * g + 0], my_g * qacc[4 * g + 1], my_g * qacc[4 * g + 2],
                         my_g * qacc[4 * g + 3]);
   }
-  auto row_of = [&](int tt) { return Rsh + ((ep[tt >> 2] >> (8 * (tt & 3))) & 0xff) * RS + col0; };
+  const uint32_t epw[4] = {ep.x, ep.y, ep.z, ep.w};
+  auto row_of = [&](int tt) { return Rsh + ((epw[tt >> 2] >> (8 * (tt & 3))) & 0xff) * RS + col0; };
   // two row buffers in turn, so the next row's loads are in flight during the
   // current row's FMAs and no registers are copied between steps
   auto load_row = [&](float4 (&buf)[4], int tt) {
