@@ -77,7 +77,7 @@ extern "C" {
 #define TV_ERR_DIMS (-2)     /* B, H or N <= 0, N > TV_MAX_NODES, or a size overflows */
 #define TV_ERR_HEAD_DIM (-3) /* d_k or d_v not in {16, 32, 64, 128} */
 #define TV_ERR_MODE (-4)     /* bad dtype or mode, or beta == NULL in GDN mode */
-#define TV_ERR_ALIAS (-5)    /* S_out overlaps an input it may not overlap */
+#define TV_ERR_ALIAS (-5)    /* an output overlaps an input it may not overlap */
 #define TV_ERR_ALGO (-6)     /* bad algo, or TV_ALGO_MFMA where it does not apply */
 #define TV_ERR_HIP_BASE (-100)
 
@@ -176,6 +176,42 @@ int tree_verify_snapshot(int B, int H, int N, int dk, int dv, int dtype, int mod
 int tree_commit_snapshot(int B, int H, int N, int dk, int dv, const float* snapshots,
                          const int32_t* parents, const int32_t* accepted, float* S_out,
                          int32_t* path_out, int32_t* status, void* stream);
+
+/*
+ * tree_commit_verify -- one decoding step with the previous step's commit
+ * deferred into this step's verification: exactly
+ *
+ *   tree_commit(B, H, N_prev, dk, dv, dtype, k_prev, alpha_prev, U_prev,
+ *               parents_prev, accepted_prev, S_in, S_out, path_out, commit_status);
+ *   tree_verify(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta, parents,
+ *               S_out, o, U, status);
+ *
+ * in one pass over the state (TreeWY abstract: only the accepted state is
+ * rebuilt, from token-level factors kept at verification; Bole auto-summary,
+ * reconstruction formula: that rebuild is the per-token factors of the path
+ * applied to the old root state).  For bf16 at d_k = d_v = 128 a single kernel
+ * reads S_in once, applies the accepted path's rank-len update in registers,
+ * writes S_out and verifies the new tree against it; other shapes run the two
+ * kernels above in stream order.  Outputs match the two calls within
+ * floating-point rounding (S_out to ~2^-24 relative, as tree_commit).
+ *
+ *   N_prev, k_prev, alpha_prev, U_prev, parents_prev, accepted_prev,
+ *   path_out, commit_status: as tree_commit's N, k, alpha, U, parents,
+ *                            accepted, path_out, status (previous tree)
+ *   S_in      [B, H, dk, dv] f32   state before the previous tree
+ *   S_out     [B, H, dk, dv] f32 OUT: committed state, the new tree's root;
+ *                                 S_out == S_in (in place) is allowed
+ *   N, q, k, v, alpha, beta, parents, o, U, status: as tree_verify (new tree)
+ * U must not overlap U_prev, and S_out must not partly overlap S_in
+ * (TV_ERR_ALIAS).  Both trees' sizes are checked as in tree_verify.
+ */
+int tree_commit_verify(int B, int H, int N_prev, int N, int dk, int dv, int dtype, int mode,
+                       const void* k_prev, const float* alpha_prev, const float* U_prev,
+                       const int32_t* parents_prev, const int32_t* accepted_prev,
+                       const float* S_in, float* S_out, int32_t* path_out, int32_t* commit_status,
+                       const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, const int32_t* parents, void* o, float* U,
+                       int32_t* status, void* stream);
 
 /* Text for a return code (negative) or a status code (0..2). Never NULL. */
 const char* tv_status_string(int code);

@@ -28,6 +28,7 @@ def lib():
     L.tree_index.argtypes = [I, I] + [P] * 5
     L.tree_verify_snapshot.argtypes = [I] * 7 + [P] * 10 + [P]
     L.tree_commit_snapshot.argtypes = [I] * 5 + [P] * 6 + [P]
+    L.tree_commit_verify.argtypes = [I] * 8 + [P] * 19
     L.tv_status_string.restype = ctypes.c_char_p
     return L
 
@@ -41,8 +42,8 @@ def declared_functions():
 def test_header_declares_expected():
     assert declared_functions() == sorted(["tree_verify", "tree_verify_algo", "tree_commit",
                                            "tree_index", "tree_verify_snapshot",
-                                           "tree_commit_snapshot", "tv_status_string",
-                                           "tv_version"])
+                                           "tree_commit_snapshot", "tree_commit_verify",
+                                           "tv_status_string", "tv_version"])
 
 
 def test_exports_every_declared_symbol(lib):
@@ -144,6 +145,31 @@ def test_snapshot_checks(lib):
     s0 = ctypes.c_void_p(0x100000)
     s1 = ctypes.c_void_p(0x100000 + 4 * 16 * 16)
     assert lib.tree_commit_snapshot(1, 1, 4, 16, 16, s0, P, P, s1, None, None, None) == TV_ERR_ALIAS
+
+
+def test_commit_verify_checks(lib):
+    P = FAKE
+    # pointers: k_prev alpha_prev U_prev parents_prev accepted_prev S_in S_out path_out
+    # commit_status | q k v alpha beta parents o U status | stream
+    def call(ptrs=None, B=1, H=1, Np=4, N=4, dk=16, dv=16, dtype=0, mode=0, **over):
+        p = [P] * 7 + [None, None] + [P] * 8 + [None] if ptrs is None else ptrs
+        for i, v in over.items():
+            p[int(i[1:])] = v
+        return lib.tree_commit_verify(B, H, Np, N, dk, dv, dtype, mode, *p, None)
+    for i in (0, 1, 2, 3, 4, 5, 6, 9, 10, 11, 12, 14, 15, 16):
+        assert call(**{f"p{i}": None}) == TV_ERR_NULL, i
+    assert call(p13=None, mode=0) == TV_ERR_MODE          # GDN needs beta
+    assert call(Np=0) == TV_ERR_DIMS
+    assert call(Np=129) == TV_ERR_DIMS
+    assert call(N=129) == TV_ERR_DIMS
+    assert call(dv=48) == TV_ERR_HEAD_DIM
+    assert call(dtype=3) == TV_ERR_MODE
+    assert call(mode=4) == TV_ERR_MODE
+    # S_out partly over S_in
+    assert call(p5=ctypes.c_void_p(0x100000), p6=ctypes.c_void_p(0x100004)) == TV_ERR_ALIAS
+    # U (new, 4 nodes x 16 floats) over U_prev
+    assert call(p2=ctypes.c_void_p(0x200000), p16=ctypes.c_void_p(0x200000 + 4 * 16 * 4 - 4)) == TV_ERR_ALIAS
+    assert call(p2=ctypes.c_void_p(0x200000 + 4 * 16 * 4 - 4), p16=ctypes.c_void_p(0x200000)) == TV_ERR_ALIAS
 
 
 def test_product_path_has_no_oracle_import():

@@ -1,0 +1,218 @@
+"""tree_commit_verify (previous step's commit fused into this step's
+verification) through the C ABI, against the fp64 oracle.
+
+Expected values: the oracle's commit of the previous tree (its literal path
+walk from the previous root state), then the oracle's verification of the new
+tree from that committed state.  Only the GPU call itself sees the previous
+step's pseudo-values U_prev, taken from the GPU's own tree_verify of the
+previous tree, as a caller would pass them.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parity import TOL, max_rel
+from tree_speculative_verification_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from tree_speculative_verification_amd import binding  # noqa: F401  (fails loudly if unbuilt)
+    torch.cuda.init()
+
+
+def _pipeline(prev, cur, inplace=False, unfused=False):
+    """GPU: verify the previous tree (for U_prev), then the fused call."""
+    import torch
+
+    from tree_speculative_verification_amd import binding as tvb
+    t0 = synth.to_torch(prev)
+    t1 = synth.to_torch(cur)
+    _, U_prev, _ = tvb.verify(t0["q"], t0["k"], t0["v"], t0["alpha"], t0["beta"], t0["parents"],
+                              t0["S_root"], mode=prev.mode)
+    S_in = t0["S_root"].clone()
+    if unfused:
+        S_out, path, cst = tvb.commit(t0["k"], t0["alpha"], U_prev, t0["parents"], t0["accepted"],
+                                      S_in, inplace=inplace)
+        o, U, st = tvb.verify(t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], t1["parents"],
+                              S_out, mode=cur.mode)
+    else:
+        S_out, path, cst, o, U, st = tvb.commit_verify(
+            t0["k"], t0["alpha"], U_prev, t0["parents"], t0["accepted"], S_in,
+            t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], t1["parents"], mode=cur.mode,
+            inplace=inplace)
+        if inplace:
+            assert S_out.data_ptr() == S_in.data_ptr()
+    torch.cuda.synchronize()
+    return dict(S=S_out.cpu().numpy(), path=path.cpu().numpy(), cst=cst.cpu().numpy(),
+                o=o.float().cpu().numpy(), U=U.cpu().numpy(), st=st.cpu().numpy())
+
+
+def _reference(prev, cur, bs=None, hs=None):
+    S_mid, cst = oracle.commit(prev.mode, prev.parents, prev.accepted, prev.k, prev.v, prev.alpha,
+                               prev.beta, prev.S_root, heads=hs, seqs=bs)
+    path, _ = oracle.accepted_paths(prev.parents, prev.accepted)
+    o, U, st = oracle.verify(cur.mode, cur.parents, cur.q, cur.k, cur.v, cur.alpha, cur.beta,
+                             S_mid, heads=hs, seqs=bs)
+    return dict(S=S_mid, path=path, cst=cst, o=o, U=U, st=st)
+
+
+def _check(prev, cur, g, bs=None, hs=None):
+    """Floating outputs within tolerance on sequences bs x heads hs; integers exact."""
+    ref = _reference(prev, cur, bs, hs)
+    np.testing.assert_array_equal(g["path"], ref["path"])
+    np.testing.assert_array_equal(g["cst"], ref["cst"])
+    ok_rows = (ref["cst"] == 0) & (ref["st"] == 0)
+    bsel = np.arange(prev.B) if bs is None else np.asarray(bs)
+    hsel = np.arange(prev.H) if hs is None else np.asarray(hs)
+    bsel = bsel[ok_rows[bsel]]
+    if cur is not None:
+        np.testing.assert_array_equal(g["st"][bsel], ref["st"][bsel])
+    tol = TOL[cur.dtype]
+    sub = np.ix_(bsel, hsel)
+    errs = dict(S=max_rel(g["S"][sub], ref["S"][sub], 0, 1),
+                U=max_rel(g["U"][sub], ref["U"][sub], 0, 1),
+                o=max_rel(g["o"][bsel][:, :, hsel], ref["o"][bsel][:, :, hsel], 0, 2))
+    assert errs["S"] <= tol["S"] and errs["U"] <= tol["U"] and errs["o"] <= tol["o"], errs
+    return errs
+
+
+def _pair(cfg, B=None, H=None, seed_cur=100):
+    prev = synth.make_inputs(cfg, B=B, H=H)
+    cur = synth.make_inputs(cfg, seed=cfg + seed_cur, B=B, H=H)
+    return prev, cur
+
+
+@pytest.mark.parametrize("cfg,B,H", [(3, None, None), (4, 4, 8), (5, 2, 4)])
+def test_fused_matches_oracle(cfg, B, H):
+    """Chain (32-node tiles), random 64-node and wide 128-node trees: all three kernel shapes."""
+    prev, cur = _pair(cfg, B, H)
+    g = _pipeline(prev, cur)
+    assert not g["st"].any() and not g["cst"].any()
+    _check(prev, cur, g)
+
+
+def test_fused_full_size_sampled():
+    """The 64-node workload at full size (B=32, H=32), in the launch shape the benchmark
+    times; sampled (sequence, head) pairs against the oracle."""
+    prev, cur = _pair(4)
+    g = _pipeline(prev, cur)
+    assert not g["st"].any() and not g["cst"].any()
+    _check(prev, cur, g, bs=[0, 13, 31], hs=[0, 17, 31])
+
+
+def test_fused_wide_tree_full_batch_sampled():
+    prev, cur = _pair(5, B=16, H=64)
+    g = _pipeline(prev, cur)
+    _check(prev, cur, g, bs=[0, 15], hs=[5, 63])
+
+
+def test_fused_inplace():
+    prev, cur = _pair(4, 2, 4)
+    g = _pipeline(prev, cur, inplace=True)
+    _check(prev, cur, g)
+
+
+def test_fused_agrees_with_two_kernels():
+    """Same inputs through tree_commit + tree_verify: states within fp32 rounding."""
+    prev, cur = _pair(4, 4, 8)
+    g1 = _pipeline(prev, cur)
+    g2 = _pipeline(prev, cur, unfused=True)
+    np.testing.assert_array_equal(g1["path"], g2["path"])
+    assert max_rel(g1["S"], g2["S"], 0, 1) <= 1e-6
+    assert max_rel(g1["U"], g2["U"], 0, 1) <= 1e-4
+    assert max_rel(g1["o"], g2["o"], 0, 2) <= 1e-2
+
+
+def _custom_pair(par_prev, acc_prev, par_cur, H=2, d=128, mode=synth.GDN, dtype=synth.BF16,
+                 seed=0):
+    prev = synth.make_custom(par_prev, acc_prev, H, d, d, mode=mode, dtype=dtype, seed=seed)
+    cur = synth.make_custom(par_cur, np.zeros(len(par_cur), np.int32), H, d, d, mode=mode,
+                            dtype=dtype, seed=seed + 1)
+    cur.S_root = prev.S_root.copy()  # unused: the new root is the committed state
+    return prev, cur
+
+
+def _chain(n):
+    return np.arange(-1, n - 1, dtype=np.int32)
+
+
+def _random(rng, n, depth=6, fan=4):
+    return synth.random_tree(rng, n, max_depth=depth, max_children=fan).astype(np.int32)
+
+
+@pytest.mark.parametrize("Np,N", [(64, 8), (8, 64), (128, 40), (20, 128), (1, 33)])
+def test_fused_tree_sizes_differ(Np, N):
+    """Previous and new trees of different sizes (and kernel shapes)."""
+    rng = np.random.default_rng(Np * 1000 + N)
+    par_p = np.stack([_random(rng, Np) for _ in range(3)])
+    par_c = np.stack([_random(rng, N) for _ in range(3)])
+    acc = rng.integers(0, Np, size=3).astype(np.int32)
+    prev, cur = _custom_pair(par_p, acc, par_c, seed=Np + N)
+    g = _pipeline(prev, cur)
+    _check(prev, cur, g)
+
+
+@pytest.mark.parametrize("Np,acc", [(40, 39), (128, 127), (128, 16), (17, 16)])
+def test_fused_long_previous_path(Np, acc):
+    """Accepted paths longer than 16 (the update runs in rounds of 16 path nodes)."""
+    par_p = np.stack([_chain(Np)] * 2)
+    rng = np.random.default_rng(Np)
+    par_c = np.stack([_random(rng, 64) for _ in range(2)])
+    prev, cur = _custom_pair(par_p, np.array([acc, acc // 2], np.int32), par_c, seed=acc)
+    g = _pipeline(prev, cur)
+    _check(prev, cur, g)
+
+
+@pytest.mark.parametrize("N", [20, 64, 100])
+def test_fused_deep_new_tree(N):
+    """New trees with paths longer than 16 take the level-scheduled solve after the
+    commit (same kernel)."""
+    rng = np.random.default_rng(N)
+    par_p = np.stack([_random(rng, 64) for _ in range(2)])
+    par_c = np.stack([_chain(N), _random(rng, N, depth=N, fan=2)])
+    prev, cur = _custom_pair(par_p, np.array([63, 10], np.int32), par_c, seed=N)
+    g = _pipeline(prev, cur)
+    _check(prev, cur, g)
+
+
+def test_fused_scalar_decay_bf16():
+    rng = np.random.default_rng(7)
+    par_p = np.stack([_random(rng, 50) for _ in range(2)])
+    par_c = np.stack([_random(rng, 30) for _ in range(2)])
+    prev, cur = _custom_pair(par_p, np.array([49, 3], np.int32), par_c,
+                             mode=synth.SCALAR_DECAY, seed=11)
+    g = _pipeline(prev, cur)
+    _check(prev, cur, g)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_fused_other_shapes(cfg):
+    """fp32 and d < 128 run the two kernels in order behind the same entry point."""
+    prev, cur = _pair(cfg)
+    g = _pipeline(prev, cur)
+    _check(prev, cur, g)
+
+
+def test_fused_bad_rows():
+    """Bad previous parents (status 1), bad accepted index (status 2, empty path),
+    bad new parents (verification status 1); the good row is still exact."""
+    rng = np.random.default_rng(3)
+    good = _random(rng, 12)
+    bad = good.copy()
+    bad[5] = 9                      # parent after the node
+    par_p = np.stack([good, bad, good, good])
+    acc = np.array([11, 4, 12, -1], np.int32)
+    par_c = np.stack([good, good, good, bad])
+    prev, cur = _custom_pair(par_p, acc, par_c, seed=5)
+    g = _pipeline(prev, cur)
+    assert list(g["cst"]) == [0, 1, 2, 2]
+    assert list(g["st"]) == [0, 0, 0, 1]
+    assert (g["path"][1:] == -1).all()
+    _check(prev.select([0], [0, 1]), cur.select([0], [0, 1]),
+           {key: val[[0]] for key, val in g.items()})

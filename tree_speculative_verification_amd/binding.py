@@ -21,7 +21,7 @@ TV_ALGO_AUTO, TV_ALGO_LEVEL, TV_ALGO_MFMA = 0, 1, 2
 TV_MAX_NODES = 128
 
 SYMBOLS = ["tree_verify", "tree_verify_algo", "tree_commit", "tree_index", "tree_verify_snapshot",
-           "tree_commit_snapshot", "tv_status_string", "tv_version"]
+           "tree_commit_snapshot", "tree_commit_verify", "tv_status_string", "tv_version"]
 
 
 class TreeVerifyError(RuntimeError):
@@ -48,6 +48,8 @@ def _load() -> ctypes.CDLL:
     lib.tree_verify_snapshot.restype = I
     lib.tree_commit_snapshot.argtypes = [I] * 5 + [P] * 6 + [P]
     lib.tree_commit_snapshot.restype = I
+    lib.tree_commit_verify.argtypes = [I] * 8 + [P] * 9 + [P] * 9 + [P]
+    lib.tree_commit_verify.restype = I
     lib.tv_status_string.argtypes = [I]
     lib.tv_status_string.restype = ctypes.c_char_p
     lib.tv_version.argtypes = []
@@ -223,3 +225,59 @@ def commit_snapshot(snapshots, parents, accepted, S_out=None, path_out=None, sta
     if rc != 0:
         raise TreeVerifyError(rc, "tree_commit_snapshot")
     return S_out, path_out, status
+
+
+def commit_verify(k_prev, alpha_prev, U_prev, parents_prev, accepted_prev, S_in,
+                  q, k, v, alpha, beta, parents, mode=TV_GDN, S_out=None, inplace=False,
+                  path_out=None, commit_status=None, o=None, U=None, status=None, stream=None):
+    """Previous step's commit fused into this step's verification.
+
+    Returns (S_out, path_out, commit_status, o, U, status): the committed state
+    [B,H,dk,dv] (the new tree's root), the previous accepted path [B,N_prev] and
+    its status, then tree_verify's outputs for the new tree against S_out.
+    """
+    B, N, H, dk = q.shape
+    Np = k_prev.shape[1]
+    dv = v.shape[3]
+    dev = q.device
+    dt = q.dtype
+    _check(k_prev, "k_prev", (B, Np, H, dk), dt, dev)
+    _check(alpha_prev, "alpha_prev", (B, Np, H), torch.float32, dev)
+    _check(U_prev, "U_prev", (B, H, Np, dv), torch.float32, dev)
+    _check(parents_prev, "parents_prev", (B, Np), torch.int32, dev)
+    _check(accepted_prev, "accepted_prev", (B,), torch.int32, dev)
+    _check(S_in, "S_in", (B, H, dk, dv), torch.float32, dev)
+    _check(q, "q", (B, N, H, dk), dt, dev)
+    _check(k, "k", (B, N, H, dk), dt, dev)
+    _check(v, "v", (B, N, H, dv), dt, dev)
+    _check(alpha, "alpha", (B, N, H), torch.float32, dev)
+    if mode == TV_GDN or beta is not None:
+        _check(beta, "beta", (B, N, H), torch.float32, dev)
+    _check(parents, "parents", (B, N), torch.int32, dev)
+    if S_out is None:
+        S_out = S_in if inplace else torch.empty_like(S_in)
+    if path_out is None:
+        path_out = torch.empty((B, Np), dtype=torch.int32, device=dev)
+    if commit_status is None:
+        commit_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    if o is None:
+        o = torch.empty((B, N, H, dv), dtype=dt, device=dev)
+    if U is None:
+        U = torch.empty((B, H, N, dv), dtype=torch.float32, device=dev)
+    if status is None:
+        status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(S_out, "S_out", (B, H, dk, dv), torch.float32, dev)
+    _check(path_out, "path_out", (B, Np), torch.int32, dev)
+    _check(commit_status, "commit_status", (B,), torch.int32, dev)
+    _check(o, "o", (B, N, H, dv), dt, dev)
+    _check(U, "U", (B, H, N, dv), torch.float32, dev)
+    _check(status, "status", (B,), torch.int32, dev)
+    rc = LIB.tree_commit_verify(B, H, Np, N, dk, dv, _dtype_code(q), mode, _ptr(k_prev),
+                                _ptr(alpha_prev), _ptr(U_prev), _ptr(parents_prev),
+                                _ptr(accepted_prev), _ptr(S_in), _ptr(S_out), _ptr(path_out),
+                                _ptr(commit_status), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                _ptr(beta), _ptr(parents), _ptr(o), _ptr(U), _ptr(status),
+                                _stream(stream))
+    if rc != 0:
+        raise TreeVerifyError(rc, "tree_commit_verify")
+    return S_out, path_out, commit_status, o, U, status

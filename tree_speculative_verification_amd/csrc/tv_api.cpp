@@ -122,6 +122,53 @@ int tree_commit_snapshot(int B, int H, int N, int dk, int dv, const float* snaps
                                              path_out, status, static_cast<hipStream_t>(stream)));
 }
 
+int tree_commit_verify(int B, int H, int N_prev, int N, int dk, int dv, int dtype, int mode,
+                       const void* k_prev, const float* alpha_prev, const float* U_prev,
+                       const int32_t* parents_prev, const int32_t* accepted_prev,
+                       const float* S_in, float* S_out, int32_t* path_out, int32_t* commit_status,
+                       const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, const int32_t* parents, void* o, float* U,
+                       int32_t* status, void* stream) {
+  if (!k_prev || !alpha_prev || !U_prev || !parents_prev || !accepted_prev || !S_in || !S_out ||
+      !q || !k || !v || !alpha || !parents || !o || !U)
+    return TV_ERR_NULL;
+  int rc = check_common(B, H, N, dk, dv, dtype);
+  if (rc) return rc;
+  rc = check_common(B, H, N_prev, dk, dv, dtype);
+  if (rc) return rc;
+  if (mode != TV_GDN && mode != TV_SCALAR_DECAY) return TV_ERR_MODE;
+  if (mode == TV_GDN && !beta) return TV_ERR_MODE;
+  const uintptr_t sbytes = (uintptr_t)B * H * dk * dv * sizeof(float);
+  const uintptr_t si = reinterpret_cast<uintptr_t>(S_in), so = reinterpret_cast<uintptr_t>(S_out);
+  if (si != so && si < so + sbytes && so < si + sbytes) return TV_ERR_ALIAS;
+  // U_prev is read while U is written
+  const uintptr_t up = reinterpret_cast<uintptr_t>(U_prev), un = reinterpret_cast<uintptr_t>(U);
+  const uintptr_t upb = (uintptr_t)B * H * N_prev * dv * sizeof(float);
+  const uintptr_t unb = (uintptr_t)B * H * N * dv * sizeof(float);
+  if (up < un + unb && un < up + upb) return TV_ERR_ALIAS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == TV_BF16 && dk == 128 && dv == 128) {
+    tv::PrevCommit pc;
+    pc.N = N_prev;
+    pc.k = static_cast<const uint16_t*>(k_prev);
+    pc.alpha = alpha_prev;
+    pc.U = U_prev;
+    pc.parents = parents_prev;
+    pc.accepted = accepted_prev;
+    pc.S_out = S_out;
+    pc.path_out = path_out;
+    pc.status = commit_status;
+    return hip_code(tv::launch_verify_mfma(B, H, N, mode, q, k, v, alpha, beta, parents, S_in, o, U,
+                                           status, st, &pc));
+  }
+  // other shapes: the two kernels in stream order
+  int err = tv::launch_commit(B, H, N_prev, dk, dv, dtype, k_prev, alpha_prev, U_prev, parents_prev,
+                              accepted_prev, S_in, S_out, path_out, commit_status, st);
+  if (err) return hip_code(err);
+  return hip_code(tv::launch_verify_level(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta,
+                                          parents, S_out, o, U, status, st));
+}
+
 const char* tv_status_string(int code) {
   switch (code) {
     case TV_OK: return "ok";
@@ -131,7 +178,7 @@ const char* tv_status_string(int code) {
     case TV_ERR_DIMS: return "bad sizes: B, H, N must be positive, N <= 128, sizes must fit";
     case TV_ERR_HEAD_DIM: return "d_k and d_v must be 16, 32, 64 or 128";
     case TV_ERR_MODE: return "bad dtype or mode, or beta is NULL in gated-delta-rule mode";
-    case TV_ERR_ALIAS: return "S_out overlaps an input buffer (other than S_out == S_root in tree_commit)";
+    case TV_ERR_ALIAS: return "an output overlaps an input it may not overlap (S_out == S_root in place is allowed)";
     case TV_ERR_ALGO: return "bad solver choice for these arguments";
   }
   if (code <= TV_ERR_HIP_BASE) return "HIP launch failed (code = -(100 + hipError_t))";

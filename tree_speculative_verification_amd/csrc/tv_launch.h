@@ -20,11 +20,27 @@ int launch_verify_level(int B, int H, int N, int dk, int dv, int dtype, int mode
                         const int32_t* parents, const float* S_root, void* o, float* U,
                         int32_t* status, hipStream_t stream);
 
-// bf16 q/k/v, d_k = d_v = 128 only.
+// The previous step's commit, applied to the state on the fly by the fused
+// verification (arrays as tree_commit takes them, N = the previous tree's size).
+struct PrevCommit {
+  int N;
+  const uint16_t* k;         // [B, N, H, 128] bf16
+  const float* alpha;        // [B, N, H]
+  const float* U;            // [B, H, N, 128]
+  const int32_t* parents;    // [B, N]
+  const int32_t* accepted;   // [B]
+  float* S_out;              // [B, H, 128, 128] committed state (may be the input state)
+  int32_t* path_out;         // [B, N] or null
+  int32_t* status;           // [B] or null
+};
+
+// bf16 q/k/v, d_k = d_v = 128 only.  With `prev` the state read is first
+// advanced by the previous step's commit, which is also written to
+// prev->S_out (S_root may equal prev->S_out).
 int launch_verify_mfma(int B, int H, int N, int mode, const void* q, const void* k, const void* v,
                        const float* alpha, const float* beta, const int32_t* parents,
                        const float* S_root, void* o, float* U, int32_t* status,
-                       hipStream_t stream);
+                       hipStream_t stream, const PrevCommit* prev = nullptr);
 
 // Per-node-snapshot baseline (tv_snapshot.hip).
 int launch_snapshot_verify(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,

@@ -181,13 +181,49 @@ __device__ __forceinline__ int rank_below(unsigned long long a0, unsigned long l
   return __popcll(a0) + __popcll(a1 & ((1ull << (j - 64)) - 1ull));
 }
 
-template <int NP, int VB>
-__global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
+// ---- helpers of the fused commit (the previous step's accepted path) ----
+
+// Register value of node n (uniform) when lane l holds nodes l and l + 64.
+__device__ __forceinline__ int node_lane_i(const int (&x)[2], int n) {
+  return n < 64 ? __builtin_amdgcn_readlane(x[0], n) : __builtin_amdgcn_readlane(x[1], n - 64);
+}
+__device__ __forceinline__ float node_lane_f(const float (&x)[2], int n) {
+  const int v = n < 64 ? __builtin_amdgcn_readlane(__float_as_int(x[0]), n)
+                       : __builtin_amdgcn_readlane(__float_as_int(x[1]), n - 64);
+  return __int_as_float(v);
+}
+__device__ __forceinline__ float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Eight floats as three bf16 words each (x = hi + mid + lo to ~2^-26 relative).
+__device__ __forceinline__ void split3_bf16(const float (&x)[8], bf16x8& h8, bf16x8& m8, bf16x8& l8) {
+  uint32_t wh[4], wm[4], wl[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float x0 = x[2 * p], x1 = x[2 * p + 1];
+    const uint32_t hw = pack_bf16x2(x0, x1);
+    const float r0 = x0 - __uint_as_float(__builtin_amdgcn_perm(0u, hw, 0x01000c0cu));
+    const float r1 = x1 - __uint_as_float(hw & 0xffff0000u);
+    const uint32_t mw = pack_bf16x2(r0, r1);
+    const float s0 = r0 - __uint_as_float(__builtin_amdgcn_perm(0u, mw, 0x01000c0cu));
+    const float s1 = r1 - __uint_as_float(mw & 0xffff0000u);
+    wh[p] = hw;
+    wm[p] = mw;
+    wl[p] = pack_bf16x2(s0, s1);
+  }
+  __builtin_memcpy(&h8, wh, 16);
+  __builtin_memcpy(&m8, wm, 16);
+  __builtin_memcpy(&l8, wl, 16);
+}
+
+template <int NP, int VB, bool FUSED>
+__global__ __launch_bounds__(kThreads, NP > 64 ? 1 : (FUSED ? 2 : 3)) void verify_mfma_kernel(
     int H, int N, int mode, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const int32_t* __restrict__ parents,
-    const float* __restrict__ S_root, uint16_t* __restrict__ o, float* __restrict__ U,
-    int32_t* __restrict__ status) {
+    const float* S_root, uint16_t* __restrict__ o, float* __restrict__ U,
+    int32_t* __restrict__ status, PrevCommit pc) {
   using Lay = MfmaLayout<NP, VB>;
   constexpr int NT = NP / 32;                 // node tiles
   constexpr int CT = VB / 32;                 // value-column tiles in the block
@@ -214,6 +250,15 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // each node's root path, one byte per node, in distance order (n, parent,
   // ...), padded with the node itself
   __shared__ __align__(16) uint4 sEd[NP];
+  // fused commit: the previous tree's accepted path, first 16 nodes
+  struct PrevPathLds {
+    float pd[16];   // D(e_t -> a)
+    uint32_t pe[4]; // e_t, one byte each
+    float gam;      // gamma_a
+    float cn;       // D at distance 16
+    int next;       // node at distance 16, or -1
+  };
+  __shared__ __align__(16) PrevPathLds spath;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -248,6 +293,38 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // there.  Wave 0 issues none of these, so nothing delays its tree build.
   uint16_t* Ksh = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Qsh = Ksh + NP * kD;
+  // Fused commit: the previous tree's parents and gates (nodes lane and
+  // lane + 64).  Wave 1 loads them before its K/Q rows and walks the accepted
+  // path while the rows are in flight.
+  int ppar[2] = {-1, -1};
+  float pal[2] = {1.f, 1.f};
+  auto load_prev_tree = [&]() {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int nd = min(lane + 64 * s, pc.N - 1);
+      ppar[s] = pc.parents[(size_t)b * pc.N + nd];
+      pal[s] = pc.alpha[(size_t)(b * pc.N + nd) * H + h];
+    }
+  };
+  // Walks 16 steps up the previous tree from `node` (uniform), D running in c:
+  // pe[t] = node at distance t, pd[t] = D(pe[t] -> a); node 0 and 0 past the end.
+  auto walk16 = [&](int& node, float& c, int (&pe)[16], float (&pd)[16]) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      if (node >= 0) {  // uniform
+        pe[t] = node;
+        pd[t] = c;
+        c = uniform_f(c * node_lane_f(pal, node));
+        node = node_lane_i(ppar, node);
+      } else {
+        pe[t] = 0;
+        pd[t] = 0.f;
+      }
+    }
+  };
+  if constexpr (FUSED) {
+    if (wave == 1) load_prev_tree();
+  }
   if (wave == 0) {
     int par[SL];
     float al[SL], be[SL];
@@ -324,39 +401,225 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       __builtin_amdgcn_global_load_lds(src, (isq ? Qsh : Ksh) + rb * 4 * kD, 16, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(kVmcntZero);  // this wave's K/Q rows have landed
+    if constexpr (FUSED) {
+      if (wave == 1) {
+        // the previous tree's accepted path (first 16 nodes) into LDS
+        bool badl = false;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int nd = lane + 64 * s;
+          badl |= nd < pc.N && (ppar[s] < -1 || ppar[s] >= nd);
+        }
+        const bool pbad = __any(badl) != 0;
+        const int pa = pc.accepted[b];
+        const bool bad_acc = pa < 0 || pa >= pc.N;
+        // a bad accepted index commits node 0's path (status 2), as tree_commit does
+        int node = pbad ? -1 : (bad_acc ? 0 : pa);
+        float c = 1.f;
+        int pe[16];
+        float pd[16];
+        walk16(node, c, pe, pd);
+        const int next = node;
+        const float cn = c;
+        for (int n2 = node; n2 >= 0; n2 = node_lane_i(ppar, n2)) c = uniform_f(c * node_lane_f(pal, n2));
+        if (lane < 16) {
+          float dsel = pd[0];
+#pragma unroll
+          for (int t = 1; t < 16; ++t) dsel = lane == t ? pd[t] : dsel;
+          spath.pd[lane] = dsel;
+        }
+        if (lane == 0) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            spath.pe[w] = pe[4 * w] | (pe[4 * w + 1] << 8) | (pe[4 * w + 2] << 16) | (pe[4 * w + 3] << 24);
+          spath.gam = c;
+          spath.cn = cn;
+          spath.next = next;
+        }
+        // status and root-first path of the previous step (one wave per sequence)
+        if (h == 0 && vb == 0) {
+          if (pc.status && lane == 0) pc.status[b] = pbad ? 1 : (bad_acc ? 2 : 0);
+          if (pc.path_out) {
+            int nd2 = (pbad || bad_acc) ? -1 : pa;
+            int m0 = -1, m1 = -1, len = 0;  // distance of node lane (lane + 64) from a
+            while (nd2 >= 0) {
+              if (lane == nd2) m0 = len;
+              if (lane + 64 == nd2) m1 = len;
+              nd2 = node_lane_i(ppar, nd2);
+              ++len;
+            }
+            int32_t* po = pc.path_out + (size_t)b * pc.N;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              const int nd = lane + 64 * s;
+              const int m = s ? m1 : m0;
+              if (nd < pc.N) {
+                if (m >= 0) po[len - 1 - m] = nd;
+                if (nd >= len) po[nd] = -1;
+              }
+            }
+          }
+        }
+      }
+    }
   }
   __syncthreads();  // tree, gates and K/Q staging visible
 
   const int Lmax = __builtin_amdgcn_readfirstlane(meta[0]);  // uniform: scalar loop bounds
   if (h == 0 && vb == 0 && tid == 0 && status) status[b] = meta[1] ? 1 : 0;
+
+  // This wave's S block: rows srow0 + 16 ks + 8 hi + i (KSTEPS steps of 16
+  // rows), column cbase + 32 ct_w + lm, straight into MFMA operand registers.
+  constexpr int KSTEPS = 8 / KS;                // 16-row k steps of this wave
+  constexpr int TL = KSTEPS / 2;                // 32-row tiles of those rows
+  const int srow0 = KS == 2 ? nt_w * 64 : 0;
+  // block base (uniform) + 32-bit lane offset in bytes: scalar-base addressing
+  const size_t sblk = (size_t)bh * kD * kD + cbase + ct_w * 32 + (size_t)srow0 * kD;
+  const uint32_t slane = 4u * (lm + akof * kD);
+  float sv[KSTEPS][8];
+  auto load_S = [&]() {
+    const char* Sb = reinterpret_cast<const char*>(S_root + sblk);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        sv[ks][i] = *reinterpret_cast<const float*>(Sb + slane + 4u * (ks * 16 + i) * kD);
+  };
+
+  // ---- fused commit of the previous step (TreeWY abstract: only the accepted
+  // state is rebuilt; Bole auto-summary, reconstruction formula) ----
+  //   S = gamma_a S_in + sum_t D(e_t -> a) k_{e_t} u_{e_t}^T
+  // over the previous tree's accepted path e_0 = a, e_1 = parent(a), ...  The
+  // rank-16 update of a wave's S block is one matrix-core product per 32-row
+  // tile (k exact in bf16, D u split into three bf16 words, accumulated onto
+  // gamma_a S in the operand registers); the block is then stored as the
+  // committed state and used as S below.  Path nodes j = 8 hi + i of a chunk
+  // of 16 belong to lane half hi.
+  // Tile (T, tau) of the update covers the wave's state rows 64 T + 2 m + tau
+  // (m = matrix-core row): its accumulator element 4 s + i of lane (column c,
+  // half hi) is then row 64 T + 16 s + 8 hi + 2 i + tau, i.e. sv[4 T + s][2 i + tau],
+  // and one 32-bit load of k at rows (2 m, 2 m + 1) feeds both tau.
+  uint32_t kpd[TL / 2][8];  // k_{e_j} at rows 64 T + 2 lm (+1), j = 8 hi + i
+  float upa[8];             // u_{e_j} at this lane's column
+  auto prev_loads = [&](const int (&ej)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      upa[i] = pc.U[((size_t)bh * pc.N + ej[i]) * kD + cbase + ct_w * 32 + lm];
+      const uint32_t* kr = reinterpret_cast<const uint32_t*>(
+          pc.k + ((size_t)(b * pc.N + ej[i]) * H + h) * kD + srow0 + 2 * lm);
+#pragma unroll
+      for (int T = 0; T < TL / 2; ++T) kpd[T][i] = kr[32 * T];
+    }
+  };
+  auto prev_apply = [&](const float (&dj)[8]) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = dj[i] * upa[i];
+    bf16x8 uh, um, ul;
+    split3_bf16(x, uh, um, ul);
+#pragma unroll
+    for (int T = 0; T < TL / 2; ++T) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        uint32_t aw[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          aw[p] = __builtin_amdgcn_perm(kpd[T][2 * p + 1], kpd[T][2 * p], tau ? 0x07060302u : 0x05040100u);
+        bf16x8 a;
+        __builtin_memcpy(&a, aw, 16);
+        f32x16 acc;
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[4 * ss + i] = sv[4 * T + ss][2 * i + tau];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, uh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, um, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ul, acc, 0, 0, 0);
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[4 * T + ss][2 * i + tau] = acc[4 * ss + i];
+      }
+    }
+  };
+  // first 16 path nodes: from the table wave 1 wrote
+  auto prev_loads0 = [&]() {
+    const uint2 w = reinterpret_cast<const uint2*>(spath.pe)[hi];
+    int ej[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ej[i] = ((i < 4 ? w.x : w.y) >> (8 * (i & 3))) & 0xff;
+    prev_loads(ej);
+  };
+  auto commit_prev = [&]() {
+    const float gam = spath.gam;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[ks][i] *= gam;
+    {
+      const float4 d0 = reinterpret_cast<const float4*>(spath.pd)[2 * hi];
+      const float4 d1 = reinterpret_cast<const float4*>(spath.pd)[2 * hi + 1];
+      const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      prev_apply(dj);
+    }
+    int node = __builtin_amdgcn_readfirstlane(spath.next);
+    if (node >= 0) {  // uniform: a path longer than 16, 16 more nodes per round
+      float c = spath.cn;
+      load_prev_tree();
+      while (node >= 0) {
+        int pe[16];
+        float pd[16];
+        walk16(node, c, pe, pd);
+        int ej[8];
+        float dj[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ej[i] = hi ? pe[8 + i] : pe[i];
+          dj[i] = hi ? pd[8 + i] : pd[i];
+        }
+        prev_loads(ej);
+        prev_apply(dj);
+      }
+    }
+    if constexpr (NT == 4) {
+      // all four waves hold the same block: every wave has its S values
+      // before one of them stores over S_in (S_out may be S_in)
+      __syncthreads();
+      if (wave != 0) return;
+    }
+    char* So = reinterpret_cast<char*>(pc.S_out + sblk);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<float*>(So + slane + 4u * (ks * 16 + i) * kD) = sv[ks][i];
+  };
+
   if (Lmax > kMaxL) {
+    if constexpr (FUSED) {
+      load_S();
+      prev_loads0();
+      commit_prev();
+      __threadfence();  // the committed block is read back by the fallback
+    }
     __syncthreads();  // the staging area becomes the fallback's tables
     TreeLds& tfb = *reinterpret_cast<TreeLds*>(smem + sizeof(LevelLds));
     build_tree(tfb, parents + (size_t)b * N, N);
     level_solve<uint16_t>(tfb, *reinterpret_cast<LevelLds*>(smem), mode, b, h, H, N, kD, kD, cbase,
-                          cbase + VB, q, k, v, alpha, beta, S_root, o, U);
+                          cbase + VB, q, k, v, alpha, beta, FUSED ? pc.S_out : S_root, o, U);
     return;
   }
 
-  // the S columns of this wave's tile straight into MFMA operand registers, and
-  // V at the positions the outputs land on; they arrive during the Gram and
+  // S and V (at the positions the outputs land on) arrive during the Gram and
   // the path solve
-  constexpr int KSTEPS = 8 / KS;                // 16-row k steps of this wave
-  float sv[KSTEPS][8];
-  {
-    const float* Sb = S_root + (size_t)bh * kD * kD + cbase + ct_w * 32 + lm +
-                      (size_t)(KS == 2 ? nt_w * 64 : 0) * kD;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sv[ks][i] = Sb[(size_t)(ks * 16 + akof + i) * kD];
-  }
+  load_S();
   uint2 vv[4];
   {
     const uint16_t* vr = v + ((size_t)(b * N + my_n) * H + h) * kD + cbase + col0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) vv[g] = *reinterpret_cast<const uint2*>(vr + 8 * g);
   }
+  if constexpr (FUSED) prev_loads0();
 
   // ---- 3. ancestor-masked Gram, transposed (lane = node) ----
   {
@@ -481,6 +744,8 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
                     e[8] | (e[9] << 8) | (e[10] << 16) | (e[11] << 24),
                     e[12] | (e[13] << 8) | (e[14] << 16) | (e[15] << 24));
   }
+
+  if constexpr (FUSED) commit_prev();
 
   // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
   // S is split into bf16 hi and lo words, two k values per word (one packed
@@ -659,26 +924,36 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
 template <int NP, int VB>
 static int launch_np_vb(int B, int H, int N, int mode, const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta, const int32_t* parents,
-                        const float* S_root, void* o, float* U, int32_t* status, hipStream_t stream) {
+                        const float* S_root, void* o, float* U, int32_t* status, hipStream_t stream,
+                        const PrevCommit* prev) {
   const long long nblocks = (long long)B * H * (kD / VB);
   if (nblocks > 0x7fffffffLL) return static_cast<int>(hipErrorInvalidConfiguration);
-  hipLaunchKernelGGL((verify_mfma_kernel<NP, VB>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                     H, N, mode, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), alpha, beta, parents, S_root,
-                     static_cast<uint16_t*>(o), U, status);
+  if (prev)
+    hipLaunchKernelGGL((verify_mfma_kernel<NP, VB, true>), dim3((unsigned)nblocks), dim3(kThreads), 0,
+                       stream, H, N, mode, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta,
+                       parents, S_root, static_cast<uint16_t*>(o), U, status, *prev);
+  else
+    hipLaunchKernelGGL((verify_mfma_kernel<NP, VB, false>), dim3((unsigned)nblocks), dim3(kThreads), 0,
+                       stream, H, N, mode, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta,
+                       parents, S_root, static_cast<uint16_t*>(o), U, status, PrevCommit{});
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_verify_mfma(int B, int H, int N, int mode, const void* q, const void* k, const void* v,
                        const float* alpha, const float* beta, const int32_t* parents,
                        const float* S_root, void* o, float* U, int32_t* status,
-                       hipStream_t stream) {
+                       hipStream_t stream, const PrevCommit* prev) {
   // node tiles x value-column tiles = 4: one output tile pair per wave
   if (N <= 32)
-    return launch_np_vb<32, 128>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status, stream);
+    return launch_np_vb<32, 128>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
+                                 stream, prev);
   if (N <= 64)
-    return launch_np_vb<64, 64>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status, stream);
-  return launch_np_vb<128, 32>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status, stream);
+    return launch_np_vb<64, 64>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
+                                stream, prev);
+  return launch_np_vb<128, 32>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
+                               stream, prev);
 }
 
 }  // namespace tv
