@@ -218,7 +218,7 @@ __device__ __forceinline__ void split3_bf16(const float (&x)[8], bf16x8& h8, bf1
 }
 
 template <int NP, int VB, bool FUSED>
-__global__ __launch_bounds__(kThreads, NP > 64 ? 1 : (FUSED ? 2 : 3)) void verify_mfma_kernel(
+__global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     int H, int N, int mode, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const int32_t* __restrict__ parents,
@@ -305,6 +305,21 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : (FUSED ? 2 : 3)) void verif
       ppar[s] = pc.parents[(size_t)b * pc.N + nd];
       pal[s] = pc.alpha[(size_t)(b * pc.N + nd) * H + h];
     }
+  };
+  // First node of the previous tree's accepted path (-1: none), uniform; the
+  // parents must be loaded.  Invalid parents: no update (status 1); a bad
+  // accepted index commits node 0's path (status 2), as tree_commit does.
+  auto prev_start = [&](bool& pbad, bool& bad_acc, int& pa) {
+    bool badl = false;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int nd = lane + 64 * s;
+      badl |= nd < pc.N && (ppar[s] < -1 || ppar[s] >= nd);
+    }
+    pbad = __any(badl) != 0;
+    pa = pc.accepted[b];
+    bad_acc = pa < 0 || pa >= pc.N;
+    return pbad ? -1 : (bad_acc ? 0 : pa);
   };
   // Walks 16 steps up the previous tree from `node` (uniform), D running in c:
   // pe[t] = node at distance t, pd[t] = D(pe[t] -> a); node 0 and 0 past the end.
@@ -404,17 +419,9 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : (FUSED ? 2 : 3)) void verif
     if constexpr (FUSED) {
       if (wave == 1) {
         // the previous tree's accepted path (first 16 nodes) into LDS
-        bool badl = false;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int nd = lane + 64 * s;
-          badl |= nd < pc.N && (ppar[s] < -1 || ppar[s] >= nd);
-        }
-        const bool pbad = __any(badl) != 0;
-        const int pa = pc.accepted[b];
-        const bool bad_acc = pa < 0 || pa >= pc.N;
-        // a bad accepted index commits node 0's path (status 2), as tree_commit does
-        int node = pbad ? -1 : (bad_acc ? 0 : pa);
+        bool pbad, bad_acc;
+        int pa;
+        int node = prev_start(pbad, bad_acc, pa);
         float c = 1.f;
         int pe[16];
         float pd[16];
@@ -471,6 +478,7 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : (FUSED ? 2 : 3)) void verif
   // This wave's S block: rows srow0 + 16 ks + 8 hi + i (KSTEPS steps of 16
   // rows), column cbase + 32 ct_w + lm, straight into MFMA operand registers.
   constexpr int KSTEPS = 8 / KS;                // 16-row k steps of this wave
+  constexpr bool kCommitEarly = NT == 1;
   constexpr int TL = KSTEPS / 2;                // 32-row tiles of those rows
   const int srow0 = KS == 2 ? nt_w * 64 : 0;
   // block base (uniform) + 32-bit lane offset in bytes: scalar-base addressing
@@ -563,22 +571,26 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : (FUSED ? 2 : 3)) void verif
       prev_apply(dj);
     }
     int node = __builtin_amdgcn_readfirstlane(spath.next);
-    if (node >= 0) {  // uniform: a path longer than 16, 16 more nodes per round
+    if (node >= 0) {  // uniform: a path longer than 16, one more node per round
       float c = spath.cn;
       load_prev_tree();
+      const int col = cbase + ct_w * 32 + lm;
       while (node >= 0) {
-        int pe[16];
-        float pd[16];
-        walk16(node, c, pe, pd);
-        int ej[8];
-        float dj[8];
+        const float u = c * pc.U[((size_t)bh * pc.N + node) * kD + col];
+        const uint4* kr = reinterpret_cast<const uint4*>(
+            pc.k + ((size_t)(b * pc.N + node) * H + h) * kD + srow0 + akof);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ej[i] = hi ? pe[8 + i] : pe[i];
-          dj[i] = hi ? pd[8 + i] : pd[i];
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const uint4 w = kr[2 * ks];  // k at rows 16 ks + 8 hi + 0..7
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[ks][2 * e] = fmaf(__uint_as_float(ws[e] << 16), u, sv[ks][2 * e]);
+            sv[ks][2 * e + 1] = fmaf(__uint_as_float(ws[e] & 0xffff0000u), u, sv[ks][2 * e + 1]);
+          }
         }
-        prev_loads(ej);
-        prev_apply(dj);
+        c = uniform_f(c * node_lane_f(pal, node));
+        node = node_lane_i(ppar, node);
       }
     }
     if constexpr (NT == 4) {
@@ -597,10 +609,51 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : (FUSED ? 2 : 3)) void verif
 
   if (Lmax > kMaxL) {
     if constexpr (FUSED) {
-      load_S();
-      prev_loads0();
-      commit_prev();
-      __threadfence();  // the committed block is read back by the fallback
+      // the previous step's commit of this block, plainly (rare path): the
+      // whole accepted path into the Gram tables (unused here), then
+      // S_out = gamma_a S_in + sum_t D_t k_t u_t^T element by element
+      int* fpath = reinterpret_cast<int*>(CkkD);
+      float* fd = CqkD;
+      load_prev_tree();
+      if (wave == 0) {
+        bool pbad, bad_acc;
+        int pa;
+        int node = prev_start(pbad, bad_acc, pa);
+        float c = 1.f;
+        int t = 0;
+        while (node >= 0) {  // uniform
+          if (lane == 0) {
+            fpath[t] = node;
+            fd[t] = c;
+          }
+          c = uniform_f(c * node_lane_f(pal, node));
+          node = node_lane_i(ppar, node);
+          ++t;
+        }
+        if (lane == 0) {
+          gsink[0] = __int_as_float(t);
+          gsink[1] = c;
+        }
+      }
+      __syncthreads();
+      const int Lp = __float_as_int(gsink[0]);
+      const float gam = gsink[1];
+      const float* Si = S_root + (size_t)bh * kD * kD;
+      float* So = pc.S_out + (size_t)bh * kD * kD;
+      for (int e = tid; e < kD * (VB / 4); e += kThreads) {
+        const int r = e / (VB / 4);
+        const int c = cbase + 4 * (e % (VB / 4));
+        float4 acc = mul4(gam, *reinterpret_cast<const float4*>(Si + r * kD + c));
+        for (int t = 0; t < Lp; ++t) {
+          const int nd = fpath[t];
+          const float kr = __uint_as_float(
+              static_cast<uint32_t>(pc.k[((size_t)(b * pc.N + nd) * H + h) * kD + r]) << 16);
+          const float4 u = *reinterpret_cast<const float4*>(pc.U + ((size_t)bh * pc.N + nd) * kD + c);
+          acc = fma4(fd[t] * kr, u, acc);
+        }
+        *reinterpret_cast<float4*>(So + r * kD + c) = acc;
+      }
+      __threadfence();  // the committed block is read back below
     }
     __syncthreads();  // the staging area becomes the fallback's tables
     TreeLds& tfb = *reinterpret_cast<TreeLds*>(smem + sizeof(LevelLds));
@@ -681,6 +734,10 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : (FUSED ? 2 : 3)) void verif
     }
   }
   __syncthreads();  // path Gram entries visible
+  // The fused commit runs where its registers fit: after the Gram when the
+  // wave holds all 128 rows of S (one node tile), else just before the
+  // contraction that consumes S.
+  if constexpr (FUSED && kCommitEarly) commit_prev();
 
   // ---- 4. path solve: lane = (node my_n, chain hi) in every wave ----
   // Distance order e_0 = n, e_1 = parent(n), ...  Chain 0 gives x (u_n = sum_t
@@ -745,7 +802,7 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : (FUSED ? 2 : 3)) void verif
                     e[12] | (e[13] << 8) | (e[14] << 16) | (e[15] << 24));
   }
 
-  if constexpr (FUSED) commit_prev();
+  if constexpr (FUSED && !kCommitEarly) commit_prev();
 
   // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
   // S is split into bf16 hi and lo words, two k values per word (one packed
