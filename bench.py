@@ -1,20 +1,25 @@
 #!/usr/bin/env python3
 """Verified tree nodes/s through one gated-delta-rule layer on one MI355X.
 
-One step = tree_verify + tree_commit over one batch of the 64-node workload
-(B=32 sequences, H=32 heads, d_k=d_v=128, bf16 q/k/v, fp32 state, a random
-64-node draft tree per sequence, accepted node uniform over nodes).  Inputs
-are seeded synthetic data, resident in HBM before timing starts.
+Workload: the 64-node tree (B=32 sequences, H=32 heads, d_k=d_v=128, bf16
+q/k/v, fp32 state, a random 64-node draft tree per sequence, accepted node
+uniform over nodes).  Inputs are seeded synthetic data, resident in HBM
+before timing starts.
 
+One step verifies one batch and commits one batch.  Two pipelines are timed:
+  * fused (the headline): one tree_commit_verify launch per step, which
+    commits an earlier batch's accepted path into its state and verifies
+    this batch's tree against the result, reading the state once;
+  * two-kernel: tree_verify + tree_commit per step.
 Cold caches without flush kernels: R copies of the input set (>= 1 GB in all,
-far above the 256 MB Infinity Cache and the L2s) are used in turn.  Step i
-verifies set i mod R and commits set (i - 2) mod R, whose pseudo-values came
-from the verify two steps earlier; so every kernel streams its operands from
-HBM, as it would with the rest of a model forward between verify and commit.
-W warm-up steps, then K timed steps between one pair of HIP events on the
-launch stream (bracketed by device synchronizations).  ms_per_step is that
-time / K; value = B*N / ms_per_step.  Per-kernel durations for the roofline
-come from K back-to-back launches of each kernel alone over the same ring.
+far above the 256 MB Infinity Cache and the L2s) are used in turn, and a
+step's commit takes the batch verified two steps earlier, so every kernel
+streams its operands from HBM, as it would with the rest of a model forward
+between verify and commit.  W warm-up steps, then K timed steps between one
+pair of HIP events on the launch stream (bracketed by device
+synchronizations).  ms_per_step is that time / K; value = B*N / ms_per_step
+of the fused pipeline.  Per-kernel durations for the roofline come from K
+back-to-back launches of each kernel over the same ring.
 
 Prints ONE JSON line.  Options: --steps K --warmup W --gpus 1 (only 1 is
 supported: the path runs on one GPU) --workload {3,4,5} --no-cpu-baseline.
@@ -40,6 +45,8 @@ METRIC = "verified tree nodes/s per GDN layer (1 GPU) + % of HBM roofline"
 KERNEL_SOURCES = {
     "verify": ["tree_speculative_verification_amd/csrc/tv_verify_mfma.hip",
                "tree_speculative_verification_amd/csrc/tv_device.h"],
+    "fused": ["tree_speculative_verification_amd/csrc/tv_verify_mfma.hip",
+              "tree_speculative_verification_amd/csrc/tv_device.h"],
     "commit": ["tree_speculative_verification_amd/csrc/tv_commit.hip",
                "tree_speculative_verification_amd/csrc/tv_device.h"],
 }
@@ -66,7 +73,9 @@ def algorithmic_bytes(bt):
     verify = B * H * verify_bh + B * (4 * N + 4)
     L = path_lengths(bt.parents, bt.accepted)
     commit = int(np.sum(H * (8 * dk * dv + L * (dk * s + 4 * dv + 4)))) + B * (4 * N + 4 + 4 + 4 * N)
-    return int(verify), int(commit), L
+    # fused: both, with the state read once (the commit's read is the verify's)
+    fused = verify + commit - B * H * 4 * dk * dv
+    return int(verify), int(commit), int(fused), L
 
 
 def sources_sha(kind):
@@ -255,6 +264,15 @@ def main(argv=None):
         tvb.commit(t["k"], t["alpha"], t["U"], t["parents"], t["accepted"], t["S_root"],
                    S_out=t["S_out"], path_out=t["path"], status=t["st_c"], stream=stream)
 
+    def fused(i):
+        p = sets[(i - 2) % R]
+        t = sets[i % R]
+        tvb.commit_verify(p["k"], p["alpha"], p["U"], p["parents"], p["accepted"], p["S_root"],
+                          t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["parents"],
+                          mode=bt.mode, S_out=t["S_out"], path_out=p["path"],
+                          commit_status=p["st_c"], o=t["o"], U=t["U"], status=t["st_v"],
+                          stream=stream)
+
     def timed(body, k):
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -268,19 +286,21 @@ def main(argv=None):
 
     for i in range(R):          # every set gets pseudo-values before its first commit
         verify(i)
-    for i in range(a.warmup):
+
+    def step2(i):
         verify(i)
         commit(i - 2)
+
+    for i in range(a.warmup):
+        step2(i)
+        fused(i)
     torch.cuda.synchronize()
     for t in sets:
         if t["st_v"].any().item() or t["st_c"].any().item():
             raise RuntimeError("device status reported bad input rows")
 
-    def step(i):
-        verify(i)
-        commit(i - 2)
-
-    ms_step, wall_ms = timed(step, a.steps)
+    ms_step, wall_ms = timed(fused, a.steps)
+    ms_two, _ = timed(step2, a.steps)
     tv_ms, _ = timed(verify, a.steps)
     tc_ms, _ = timed(commit, a.steps)
 
@@ -290,15 +310,17 @@ def main(argv=None):
         base = snapshot_baseline(tvb, sets, R, bt, stream, timed, a.steps, ms_step, snap_bytes)
 
     value = B * N / (ms_step * 1e-3)
-    vbytes, cbytes, L = algorithmic_bytes(bt)
+    vbytes, cbytes, fbytes, L = algorithmic_bytes(bt)
     kern = {}
-    for name, ms, nbytes in (("verify", tv_ms, vbytes), ("commit", tc_ms, cbytes)):
+    for name, ms, nbytes in (("fused", ms_step, fbytes), ("verify", tv_ms, vbytes),
+                             ("commit", tc_ms, cbytes)):
         gbs = nbytes / (ms * 1e-3) / 1e9
         kern[name] = {"mean_us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
                       "frac": round(gbs / HBM_PEAK_GBS, 4),
                       "traffic": measured_traffic(name, a.workload)}
-    dom = "verify" if tv_ms >= tc_ms else "commit"
-    combined_gbs = (vbytes + cbytes) / (ms_step * 1e-3) / 1e9
+    kern["fused"]["entry"] = "tree_commit_verify (one launch per step)"
+    dom = "fused"
+    combined_gbs = (vbytes + cbytes) / (ms_two * 1e-3) / 1e9
     snap = B * H * N * dk * dv * 4
     u_only = B * H * N * dv * 4
     u_k_g = B * H * N * (4 * dv + (2 if bt.dtype == synth.BF16 else 4) * dk + 4)
@@ -310,6 +332,8 @@ def main(argv=None):
         "config": {"workload": synth.CONFIG_NAMES[a.workload], "B": B, "H": H, "N": N,
                    "d_k": dk, "d_v": dv, "qkv": "bf16", "state": "fp32", "layer": "gated delta rule",
                    "mean_path_len": round(float(L.mean()), 3),
+                   "pipeline": "fused: one tree_commit_verify launch per step (commit of the "
+                               "batch verified 2 steps earlier + verify of this batch)",
                    "timing": f"HIP events around K steps on the launch stream; ring of {R} input "
                              "copies (>= 1 GB) so every kernel reads cold data; commit lags verify "
                              "by 2 steps"},
@@ -317,9 +341,12 @@ def main(argv=None):
                      "unit": "GB/s", "frac": kern[dom]["frac"], "traffic": kern[dom]["traffic"],
                      "kernel": dom},
         "kernels": kern,
-        "verify_plus_commit": {"achieved_GBs": round(combined_gbs, 1),
-                               "frac": round(combined_gbs / HBM_PEAK_GBS, 4),
-                               "algorithmic_bytes": vbytes + cbytes},
+        "two_kernel_pipeline": {"ms_per_step": round(ms_two, 5),
+                                "nodes_per_s": round(B * N / (ms_two * 1e-3), 1),
+                                "achieved_GBs": round(combined_gbs, 1),
+                                "frac": round(combined_gbs / HBM_PEAK_GBS, 4),
+                                "algorithmic_bytes": vbytes + cbytes,
+                                "fused_speedup": round(ms_two / ms_step, 3)},
         "wall_ms_per_step": round(wall_ms, 5),
         "transient_state_bytes": {"per_node_snapshots": snap, "U_only": u_only,
                                   "U_plus_K_and_gates": u_k_g,

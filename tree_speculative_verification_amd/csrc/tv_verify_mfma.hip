@@ -250,15 +250,19 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // each node's root path, one byte per node, in distance order (n, parent,
   // ...), padded with the node itself
   __shared__ __align__(16) uint4 sEd[NP];
-  // fused commit: the previous tree's accepted path, first 16 nodes
+  // fused commit: the previous tree's accepted path (first 16 nodes)
   struct PrevPathLds {
-    float pd[16];   // D(e_t -> a)
-    uint32_t pe[4]; // e_t, one byte each
+    float pd[16];   // D(e_t -> a), 0 past the end
     float gam;      // gamma_a
     float cn;       // D at distance 16
     int next;       // node at distance 16, or -1
   };
   __shared__ __align__(16) PrevPathLds spath;
+  // fused commit: k rows [16][128] bf16 and u columns [16][VB] f32 of those
+  // nodes, staged by wave 1; in XW (unused until the path solve) where it fits
+  constexpr int kStageBytes = 16 * kD * 2 + 16 * VB * 4;
+  constexpr bool kStageInXW = (int)sizeof(float2) * kMaxL * NP >= kStageBytes;
+  __shared__ __align__(16) unsigned char pstage[(FUSED && !kStageInXW) ? kStageBytes : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -293,9 +297,11 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // there.  Wave 0 issues none of these, so nothing delays its tree build.
   uint16_t* Ksh = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Qsh = Ksh + NP * kD;
+  unsigned char* const Pst = kStageInXW ? reinterpret_cast<unsigned char*>(XW) : pstage;
   // Fused commit: the previous tree's parents and gates (nodes lane and
-  // lane + 64).  Wave 1 loads them before its K/Q rows and walks the accepted
-  // path while the rows are in flight.
+  // lane + 64).  Wave 1 (which stages no K/Q rows then) loads them, walks the
+  // accepted path and stages its k rows and u columns while wave 0 builds the
+  // tree.
   int ppar[2] = {-1, -1};
   float pal[2] = {1.f, 1.f};
   auto load_prev_tree = [&]() {
@@ -321,20 +327,28 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     bad_acc = pa < 0 || pa >= pc.N;
     return pbad ? -1 : (bad_acc ? 0 : pa);
   };
-  // Walks 16 steps up the previous tree from `node` (uniform), D running in c:
-  // pe[t] = node at distance t, pd[t] = D(pe[t] -> a); node 0 and 0 past the end.
-  auto walk16 = [&](int& node, float& c, int (&pe)[16], float (&pd)[16]) {
+  // Walks 16 steps up the previous tree from `node` (uniform), D running in c,
+  // with scalar selects only; lane t < 16 keeps the node at distance t and its
+  // D(node -> a) (node 0 and 0 past the end).
+  auto walk16 = [&](int& node, float& c, int& my_e, float& my_d) {
+    my_e = 0;
+    my_d = 0.f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      if (node >= 0) {  // uniform
-        pe[t] = node;
-        pd[t] = c;
-        c = uniform_f(c * node_lane_f(pal, node));
-        node = node_lane_i(ppar, node);
-      } else {
-        pe[t] = 0;
-        pd[t] = 0.f;
+      const bool live = node >= 0;  // uniform
+      const int nc = live ? node : 0;
+      if (lane == t) {
+        my_e = nc;
+        my_d = live ? c : 0.f;
       }
+      const int lo = nc & 63;
+      const int p0 = __builtin_amdgcn_readlane(ppar[0], lo);
+      const int p1 = __builtin_amdgcn_readlane(ppar[1], lo);
+      const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pal[0]), lo));
+      const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pal[1]), lo));
+      const float cn = uniform_f(c * (nc < 64 ? a0 : a1));
+      c = live ? cn : c;
+      node = live ? (nc < 64 ? p0 : p1) : -1;
     }
   };
   if constexpr (FUSED) {
@@ -404,9 +418,71 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       meta[0] = Lmax;
       meta[1] = bad;
     }
+  } else if (FUSED && wave == 1) {
+    // the previous tree's accepted path (first 16 nodes) into LDS
+    bool pbad, bad_acc;
+    int pa;
+    int node = prev_start(pbad, bad_acc, pa);
+    float c = 1.f;
+    int my_e;
+    float my_d;
+    walk16(node, c, my_e, my_d);
+    const int next = node;
+    const float cn = c;
+    for (int n2 = node; n2 >= 0; n2 = node_lane_i(ppar, n2)) c = uniform_f(c * node_lane_f(pal, n2));
+    if (lane < 16) spath.pd[lane] = my_d;
+    if (lane == 0) {
+      spath.gam = c;
+      spath.cn = cn;
+      spath.next = next;
+    }
+    // Stage their k rows ([j][128] bf16, 4 rows an instruction) and u columns
+    // ([j][VB] f32) with LDS DMA, 16 bytes a lane; every source node first
+    // (cross-lane reads), then every copy, so no copy waits on another.
+    constexpr int CPJ = VB / 4;  // 16-byte chunks of a u row
+    int ek[4], eu[VB / 16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ek[r] = __shfl(my_e, 4 * r + (lane >> 4));
+#pragma unroll
+    for (int r = 0; r < VB / 16; ++r) eu[r] = __shfl(my_e, (64 / CPJ) * r + lane / CPJ);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      __builtin_amdgcn_global_load_lds(pc.k + ((size_t)(b * pc.N + ek[r]) * H + h) * kD + (lane & 15) * 8,
+                                       Pst + r * 1024, 16, 0, 0);
+#pragma unroll
+    for (int r = 0; r < VB / 16; ++r)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const uint16_t*>(pc.U + ((size_t)bh * pc.N + eu[r]) * kD + cbase + (lane % CPJ) * 4),
+          Pst + 16 * kD * 2 + r * 1024, 16, 0, 0);
+    // status and root-first path of the previous step (one wave per sequence)
+    if (h == 0 && vb == 0) {
+      if (pc.status && lane == 0) pc.status[b] = pbad ? 1 : (bad_acc ? 2 : 0);
+      if (pc.path_out) {
+        int nd2 = (pbad || bad_acc) ? -1 : pa;
+        int m0 = -1, m1 = -1, len = 0;  // distance of node lane (lane + 64) from a
+        while (nd2 >= 0) {
+          if (lane == nd2) m0 = len;
+          if (lane + 64 == nd2) m1 = len;
+          nd2 = node_lane_i(ppar, nd2);
+          ++len;
+        }
+        int32_t* po = pc.path_out + (size_t)b * pc.N;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int nd = lane + 64 * s;
+          const int m = s ? m1 : m0;
+          if (nd < pc.N) {
+            if (m >= 0) po[len - 1 - m] = nd;
+            if (nd >= len) po[nd] = -1;
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);  // the staged rows have landed
   } else {
     const int slot = lane & 15;
-    for (int blk = wave - 1; blk < NP / 2; blk += 3) {  // 4-row blocks: K, then Q
+    // 4-row blocks: K, then Q (waves 2 and 3 only when wave 1 stages the commit)
+    for (int blk = wave - (FUSED ? 2 : 1); blk < NP / 2; blk += (FUSED ? 2 : 3)) {
       const bool isq = blk >= NP / 4;
       const int rb = isq ? blk - NP / 4 : blk;
       const int row = rb * 4 + (lane >> 4);
@@ -416,59 +492,6 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       __builtin_amdgcn_global_load_lds(src, (isq ? Qsh : Ksh) + rb * 4 * kD, 16, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(kVmcntZero);  // this wave's K/Q rows have landed
-    if constexpr (FUSED) {
-      if (wave == 1) {
-        // the previous tree's accepted path (first 16 nodes) into LDS
-        bool pbad, bad_acc;
-        int pa;
-        int node = prev_start(pbad, bad_acc, pa);
-        float c = 1.f;
-        int pe[16];
-        float pd[16];
-        walk16(node, c, pe, pd);
-        const int next = node;
-        const float cn = c;
-        for (int n2 = node; n2 >= 0; n2 = node_lane_i(ppar, n2)) c = uniform_f(c * node_lane_f(pal, n2));
-        if (lane < 16) {
-          float dsel = pd[0];
-#pragma unroll
-          for (int t = 1; t < 16; ++t) dsel = lane == t ? pd[t] : dsel;
-          spath.pd[lane] = dsel;
-        }
-        if (lane == 0) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            spath.pe[w] = pe[4 * w] | (pe[4 * w + 1] << 8) | (pe[4 * w + 2] << 16) | (pe[4 * w + 3] << 24);
-          spath.gam = c;
-          spath.cn = cn;
-          spath.next = next;
-        }
-        // status and root-first path of the previous step (one wave per sequence)
-        if (h == 0 && vb == 0) {
-          if (pc.status && lane == 0) pc.status[b] = pbad ? 1 : (bad_acc ? 2 : 0);
-          if (pc.path_out) {
-            int nd2 = (pbad || bad_acc) ? -1 : pa;
-            int m0 = -1, m1 = -1, len = 0;  // distance of node lane (lane + 64) from a
-            while (nd2 >= 0) {
-              if (lane == nd2) m0 = len;
-              if (lane + 64 == nd2) m1 = len;
-              nd2 = node_lane_i(ppar, nd2);
-              ++len;
-            }
-            int32_t* po = pc.path_out + (size_t)b * pc.N;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const int nd = lane + 64 * s;
-              const int m = s ? m1 : m0;
-              if (nd < pc.N) {
-                if (m >= 0) po[len - 1 - m] = nd;
-                if (nd >= len) po[nd] = -1;
-              }
-            }
-          }
-        }
-      }
-    }
   }
   __syncthreads();  // tree, gates and K/Q staging visible
 
@@ -478,7 +501,6 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // This wave's S block: rows srow0 + 16 ks + 8 hi + i (KSTEPS steps of 16
   // rows), column cbase + 32 ct_w + lm, straight into MFMA operand registers.
   constexpr int KSTEPS = 8 / KS;                // 16-row k steps of this wave
-  constexpr bool kCommitEarly = NT == 1;
   constexpr int TL = KSTEPS / 2;                // 32-row tiles of those rows
   const int srow0 = KS == 2 ? nt_w * 64 : 0;
   // block base (uniform) + 32-bit lane offset in bytes: scalar-base addressing
@@ -509,16 +531,6 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // and one 32-bit load of k at rows (2 m, 2 m + 1) feeds both tau.
   uint32_t kpd[TL / 2][8];  // k_{e_j} at rows 64 T + 2 lm (+1), j = 8 hi + i
   float upa[8];             // u_{e_j} at this lane's column
-  auto prev_loads = [&](const int (&ej)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      upa[i] = pc.U[((size_t)bh * pc.N + ej[i]) * kD + cbase + ct_w * 32 + lm];
-      const uint32_t* kr = reinterpret_cast<const uint32_t*>(
-          pc.k + ((size_t)(b * pc.N + ej[i]) * H + h) * kD + srow0 + 2 * lm);
-#pragma unroll
-      for (int T = 0; T < TL / 2; ++T) kpd[T][i] = kr[32 * T];
-    }
-  };
   auto prev_apply = [&](const float (&dj)[8]) {
     float x[8];
 #pragma unroll
@@ -550,14 +562,6 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       }
     }
   };
-  // first 16 path nodes: from the table wave 1 wrote
-  auto prev_loads0 = [&]() {
-    const uint2 w = reinterpret_cast<const uint2*>(spath.pe)[hi];
-    int ej[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ej[i] = ((i < 4 ? w.x : w.y) >> (8 * (i & 3))) & 0xff;
-    prev_loads(ej);
-  };
   auto commit_prev = [&]() {
     const float gam = spath.gam;
 #pragma unroll
@@ -565,6 +569,16 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) sv[ks][i] *= gam;
     {
+      // first 16 path nodes from the rows wave 1 staged
+      const uint16_t* Ks = reinterpret_cast<const uint16_t*>(Pst);
+      const float* Us = reinterpret_cast<const float*>(Pst + 16 * kD * 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        upa[i] = Us[(8 * hi + i) * VB + ct_w * 32 + lm];
+#pragma unroll
+        for (int T = 0; T < TL / 2; ++T)
+          kpd[T][i] = *reinterpret_cast<const uint32_t*>(Ks + (8 * hi + i) * kD + srow0 + 64 * T + 2 * lm);
+      }
       const float4 d0 = reinterpret_cast<const float4*>(spath.pd)[2 * hi];
       const float4 d1 = reinterpret_cast<const float4*>(spath.pd)[2 * hi + 1];
       const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
@@ -672,7 +686,6 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) vv[g] = *reinterpret_cast<const uint2*>(vr + 8 * g);
   }
-  if constexpr (FUSED) prev_loads0();
 
   // ---- 3. ancestor-masked Gram, transposed (lane = node) ----
   {
@@ -734,10 +747,10 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     }
   }
   __syncthreads();  // path Gram entries visible
-  // The fused commit runs where its registers fit: after the Gram when the
-  // wave holds all 128 rows of S (one node tile), else just before the
-  // contraction that consumes S.
-  if constexpr (FUSED && kCommitEarly) commit_prev();
+  if constexpr (FUSED) {
+    commit_prev();
+    if constexpr (kStageInXW) __syncthreads();  // staged rows read; the path solve writes XW
+  }
 
   // ---- 4. path solve: lane = (node my_n, chain hi) in every wave ----
   // Distance order e_0 = n, e_1 = parent(n), ...  Chain 0 gives x (u_n = sum_t
@@ -801,8 +814,6 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
                     e[8] | (e[9] << 8) | (e[10] << 16) | (e[11] << 24),
                     e[12] | (e[13] << 8) | (e[14] << 16) | (e[15] << 24));
   }
-
-  if constexpr (FUSED && !kCommitEarly) commit_prev();
 
   // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
   // S is split into bf16 hi and lo words, two k values per word (one packed
