@@ -304,7 +304,9 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   // tree.
   int ppar[2] = {-1, -1};
   float pal[2] = {1.f, 1.f};
+  int pacc = 0;  // the previous accepted node
   auto load_prev_tree = [&]() {
+    pacc = pc.accepted[b];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int nd = min(lane + 64 * s, pc.N - 1);
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       badl |= nd < pc.N && (ppar[s] < -1 || ppar[s] >= nd);
     }
     pbad = __any(badl) != 0;
-    pa = pc.accepted[b];
+    pa = pacc;
     bad_acc = pa < 0 || pa >= pc.N;
     return pbad ? -1 : (bad_acc ? 0 : pa);
   };
@@ -333,23 +335,33 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   auto walk16 = [&](int& node, float& c, int& my_e, float& my_d) {
     my_e = 0;
     my_d = 0.f;
+    auto steps = [&](auto two) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const bool live = node >= 0;  // uniform
-      const int nc = live ? node : 0;
-      if (lane == t) {
-        my_e = nc;
-        my_d = live ? c : 0.f;
+      for (int t = 0; t < 16; ++t) {
+        const bool live = node >= 0;  // uniform
+        const int nc = live ? node : 0;
+        if (lane == t) {
+          my_e = nc;
+          my_d = live ? c : 0.f;
+        }
+        const int lo = nc & 63;
+        int p = __builtin_amdgcn_readlane(ppar[0], lo);
+        float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pal[0]), lo));
+        if constexpr (decltype(two)::value) {
+          const int p1 = __builtin_amdgcn_readlane(ppar[1], lo);
+          const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pal[1]), lo));
+          p = nc < 64 ? p : p1;
+          a = nc < 64 ? a : a1;
+        }
+        const float cn = uniform_f(c * a);
+        c = live ? cn : c;
+        node = live ? p : -1;
       }
-      const int lo = nc & 63;
-      const int p0 = __builtin_amdgcn_readlane(ppar[0], lo);
-      const int p1 = __builtin_amdgcn_readlane(ppar[1], lo);
-      const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pal[0]), lo));
-      const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pal[1]), lo));
-      const float cn = uniform_f(c * (nc < 64 ? a0 : a1));
-      c = live ? cn : c;
-      node = live ? (nc < 64 ? p0 : p1) : -1;
-    }
+    };
+    if (pc.N > 64)  // uniform
+      steps(std::integral_constant<bool, true>{});
+    else
+      steps(std::integral_constant<bool, false>{});
   };
   if constexpr (FUSED) {
     if (wave == 1) load_prev_tree();
@@ -607,18 +619,18 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
         node = node_lane_i(ppar, node);
       }
     }
-    if constexpr (NT == 4) {
-      // all four waves hold the same block: every wave has its S values
-      // before one of them stores over S_in (S_out may be S_in)
-      __syncthreads();
-      if (wave != 0) return;
-    }
+  };
+  // The committed block goes out during the contraction, one 16-row step at a
+  // time just before that step is split (its registers are live until then
+  // anyway).  With four node tiles every wave holds the same block and wave 0
+  // stores it; all waves have their S values by then (they passed the barrier
+  // after the update), so S_out may be S_in.
+  auto store_committed = [&](int ks) {
+    if (NT == 4 && wave != 0) return;  // uniform
     char* So = reinterpret_cast<char*>(pc.S_out + sblk);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<float*>(So + slane + 4u * (ks * 16 + i) * kD) = sv[ks][i];
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<float*>(So + slane + 4u * (ks * 16 + i) * kD) = sv[ks][i];
   };
 
   if (Lmax > kMaxL) {
@@ -749,7 +761,9 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   __syncthreads();  // path Gram entries visible
   if constexpr (FUSED) {
     commit_prev();
-    if constexpr (kStageInXW) __syncthreads();  // staged rows read; the path solve writes XW
+    // staged rows read (the path solve writes XW); with four node tiles, also
+    // every wave's S values are in before wave 0 stores over S_in
+    if constexpr (kStageInXW || NT == 4) __syncthreads();
   }
 
   // ---- 4. path solve: lane = (node my_n, chain hi) in every wave ----
@@ -844,6 +858,7 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     const uint16_t* Qn = Qsh + (nt_w * 32 + lm) * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
+      if constexpr (FUSED) store_committed(ks);
       bf16x8 shi, slo;
       split(ks, shi, slo);
       const int so = kq_slot(lm, 2 * ks + hi) * 8;
@@ -870,6 +885,7 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     const uint16_t* Qo = Qsh + ((1 - nt_w) * 32 + lm) * kD;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      if constexpr (FUSED) store_committed(ks);
       bf16x8 shi, slo;
       split(ks, shi, slo);
       const int so = kq_slot(lm, nt_w * 8 + 2 * ks + hi) * 8;
