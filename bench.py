@@ -113,18 +113,19 @@ def _oracle_seq(b):
     return b
 
 
-def cpu_baseline(bt, max_seqs):
+def cpu_baseline(bt, max_seqs, reps):
     """The fp64 oracle (as it stands) over whole sequences, one process per core.
 
-    Runs before the GPU is touched (the pool forks).  Returns nodes/s scaled to
-    the metric: sequences done * N / wall seconds.
+    Runs before the GPU is touched (the pool forks).  `reps` passes over the
+    sequences.  Returns nodes/s scaled to the metric: sequences done * N / wall
+    seconds.
     """
     global _CPU_BATCH
     import multiprocessing as mp
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"
     _CPU_BATCH = bt
-    seqs = list(range(min(bt.B, max_seqs)))
+    seqs = list(range(min(bt.B, max_seqs))) * reps
     cores = min(len(os.sched_getaffinity(0)), 16, len(seqs))
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
@@ -141,9 +142,10 @@ def cpu_baseline(bt, max_seqs):
     except OSError:
         pass
     return {"value": len(seqs) * bt.N / wall, "unit": "nodes/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(seqs)} of {bt.B} sequences x all {bt.H} heads of the same workload "
-                      f"(fp64 token-by-token path walk, verify + commit), wall {wall:.2f} s on "
-                      f"{cores} worker processes, 1 BLAS thread each; {cpu_model}"}
+            "sample": f"{len(seqs) // reps} of {bt.B} sequences x all {bt.H} heads of the same "
+                      f"workload, {reps} passes (fp64 token-by-token path walk, verify + commit), "
+                      f"wall {wall:.2f} s on {cores} worker processes, 1 BLAS thread each; "
+                      f"{cpu_model}"}
 
 
 # --------------------------------------------------------------- GPU timing
@@ -212,6 +214,8 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--cpu-reps", type=int, default=3,
+                    help="passes of the CPU oracle over the sampled sequences")
     ap.add_argument("--no-snapshot-baseline", action="store_true",
                     help="skip timing the per-node-snapshot baseline kernels")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -230,7 +234,7 @@ def main(argv=None):
         return 0
 
     bt = synth.make_inputs(a.workload)
-    cpu = None if a.no_cpu_baseline else cpu_baseline(bt, a.cpu_seqs)
+    cpu = None if a.no_cpu_baseline else cpu_baseline(bt, a.cpu_seqs, a.cpu_reps)
 
     import torch
     from tree_speculative_verification_amd import binding as tvb
