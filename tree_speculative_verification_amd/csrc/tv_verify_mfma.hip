@@ -17,8 +17,9 @@
 // o_n = gamma_n QS_n + w.R_path with x, w from one backward substitution of
 // length len(n) (x for e_last, w for the read-out row).
 //
-// One workgroup per (b, h, block of VB value columns); four waves, wave w owns
-// node tile w / CT and value-column tile w % CT (NT * CT = 4):
+// One workgroup per (b, h, block of VB value columns); one wave per (node
+// tile, value-column tile) pair, NT * CT of them (four, or eight for the
+// 128-node shape):
 //   1. loads, small ones first: parents and gates, K and Q rows (staged in
 //      LDS), the wave's 32 columns of S_root straight into MFMA operand
 //      registers, and V at the positions the outputs land on;
@@ -217,8 +218,12 @@ __device__ __forceinline__ void split3_bf16(const float (&x)[8], bf16x8& h8, bf1
   __builtin_memcpy(&l8, wl, 16);
 }
 
+// Waves of a workgroup: one per (node tile, value-column tile) pair.
+template <int NP, int VB>
+constexpr int mfma_waves() { return (NP / 32) * (VB / 32); }
+
 template <int NP, int VB, bool FUSED>
-__global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
+__global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void verify_mfma_kernel(
     int H, int N, int mode, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const int32_t* __restrict__ parents,
@@ -227,11 +232,13 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   using Lay = MfmaLayout<NP, VB>;
   constexpr int NT = NP / 32;                 // node tiles
   constexpr int CT = VB / 32;                 // value-column tiles in the block
-  static_assert(NT * CT == 4, "one (node tile, column tile) pair per wave");
+  constexpr int NW = NT * CT;                 // waves
+  constexpr int NTH = 64 * NW;                // threads
+  static_assert(NW == 4 || NW == 8, "one (node tile, column tile) pair per wave");
   constexpr int NVB = kD / VB;
   constexpr int SL = NP > 64 ? 2 : 1;         // tree nodes per lane
   constexpr int NG = NT * (NT + 1);           // lower-triangular blocks of K K^T and K Q^T
-  constexpr int GPW = (NG + 3) / 4;
+  constexpr int GPW = (NG + NW - 1) / NW;
   constexpr int RS = Lay::RS;
 
   __shared__ __align__(16) unsigned char smem[Lay::bytes];
@@ -494,7 +501,7 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   } else {
     const int slot = lane & 15;
     // 4-row blocks: K, then Q (waves 2 and 3 only when wave 1 stages the commit)
-    for (int blk = wave - (FUSED ? 2 : 1); blk < NP / 2; blk += (FUSED ? 2 : 3)) {
+    for (int blk = wave - (FUSED ? 2 : 1); blk < NP / 2; blk += NW - (FUSED ? 2 : 1)) {
       const bool isq = blk >= NP / 4;
       const int rb = isq ? blk - NP / 4 : blk;
       const int row = rb * 4 + (lane >> 4);
@@ -622,11 +629,12 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   };
   // The committed block goes out during the contraction, one 16-row step at a
   // time just before that step is split (its registers are live until then
-  // anyway).  With four node tiles every wave holds the same block and wave 0
-  // stores it; all waves have their S values by then (they passed the barrier
-  // after the update), so S_out may be S_in.
+  // anyway).  With more than one node tile and no d_k split (the 128-node
+  // shape) the waves of a column tile hold the same block and the one of node
+  // tile 0 stores it; all waves have their S values by then (they passed the
+  // barrier after the update), so S_out may be S_in.
   auto store_committed = [&](int ks) {
-    if (NT == 4 && wave != 0) return;  // uniform
+    if (KS == 1 && NT > 1 && nt_w != 0) return;  // uniform
     char* So = reinterpret_cast<char*>(pc.S_out + sblk);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -666,7 +674,7 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
       const float gam = gsink[1];
       const float* Si = S_root + (size_t)bh * kD * kD;
       float* So = pc.S_out + (size_t)bh * kD * kD;
-      for (int e = tid; e < kD * (VB / 4); e += kThreads) {
+      for (int e = tid; e < kD * (VB / 4); e += NTH) {
         const int r = e / (VB / 4);
         const int c = cbase + 4 * (e % (VB / 4));
         float4 acc = mul4(gam, *reinterpret_cast<const float4*>(Si + r * kD + c));
@@ -705,7 +713,7 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
     int tnt[GPW], tjt[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-      int rem = wave + 4 * i, nt2 = -1, jt = 0;
+      int rem = wave + NW * i, nt2 = -1, jt = 0;
       for (int r = 0; r < 2 * NT; ++r) {
         const int cnt = (r % NT) + 1;
         if (rem >= 0 && rem < cnt) {
@@ -761,9 +769,10 @@ __global__ __launch_bounds__(kThreads, NP > 64 ? 1 : 3) void verify_mfma_kernel(
   __syncthreads();  // path Gram entries visible
   if constexpr (FUSED) {
     commit_prev();
-    // staged rows read (the path solve writes XW); with four node tiles, also
-    // every wave's S values are in before wave 0 stores over S_in
-    if constexpr (kStageInXW || NT == 4) __syncthreads();
+    // staged rows read (the path solve writes XW); where several waves hold
+    // the same block, also every wave's S values are in before one of them
+    // stores over S_in
+    if constexpr (kStageInXW || (KS == 1 && NT > 1)) __syncthreads();
   }
 
   // ---- 4. path solve: lane = (node my_n, chain hi) in every wave ----
@@ -1013,12 +1022,14 @@ static int launch_np_vb(int B, int H, int N, int mode, const void* q, const void
   const long long nblocks = (long long)B * H * (kD / VB);
   if (nblocks > 0x7fffffffLL) return static_cast<int>(hipErrorInvalidConfiguration);
   if (prev)
-    hipLaunchKernelGGL((verify_mfma_kernel<NP, VB, true>), dim3((unsigned)nblocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((verify_mfma_kernel<NP, VB, true>), dim3((unsigned)nblocks),
+                       dim3((64 * mfma_waves<NP, VB>())), 0,
                        stream, H, N, mode, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta,
                        parents, S_root, static_cast<uint16_t*>(o), U, status, *prev);
   else
-    hipLaunchKernelGGL((verify_mfma_kernel<NP, VB, false>), dim3((unsigned)nblocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((verify_mfma_kernel<NP, VB, false>), dim3((unsigned)nblocks),
+                       dim3((64 * mfma_waves<NP, VB>())), 0,
                        stream, H, N, mode, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta,
                        parents, S_root, static_cast<uint16_t*>(o), U, status, PrevCommit{});
@@ -1029,14 +1040,14 @@ int launch_verify_mfma(int B, int H, int N, int mode, const void* q, const void*
                        const float* alpha, const float* beta, const int32_t* parents,
                        const float* S_root, void* o, float* U, int32_t* status,
                        hipStream_t stream, const PrevCommit* prev) {
-  // node tiles x value-column tiles = 4: one output tile pair per wave
+  // one wave per (node tile, value-column tile): 4 waves up to 64 nodes, 8 above
   if (N <= 32)
     return launch_np_vb<32, 128>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
                                  stream, prev);
   if (N <= 64)
     return launch_np_vb<64, 64>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
                                 stream, prev);
-  return launch_np_vb<128, 32>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
+  return launch_np_vb<128, 64>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
                                stream, prev);
 }
 
