@@ -45,7 +45,8 @@
  *   - Preconditions not checked: finite inputs, alpha in (0, 1]; in GDN mode
  *     ||k_n|| <= 1 keeps (I - beta k k^T) non-expansive.
  *   - q is used as given: an attention scale is folded in by the caller.
- *   - N <= TV_MAX_NODES; trees of any shape up to that size are accepted.
+ *   - N <= TV_MAX_NODES; trees of any shape and depth up to that size are
+ *     accepted (the per-node-snapshot baseline takes N <= 128).
  */
 #ifndef TREE_VERIFY_H
 #define TREE_VERIFY_H
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TV_MAX_NODES 128
+#define TV_MAX_NODES 512
 
 /* dtype of q, k, v and o */
 #define TV_F32 0
@@ -67,14 +68,20 @@ extern "C" {
 #define TV_SCALAR_DECAY 1
 
 /* tree_verify_algo: which kernel solves the tree */
-#define TV_ALGO_AUTO 0  /* matrix-core path where it applies, else level-scheduled */
-#define TV_ALGO_LEVEL 1 /* level-scheduled forward substitution, fp32 FMA, any d */
-#define TV_ALGO_MFMA 2  /* bf16 matrix cores + per-node path solve; bf16, d_k = d_v = 128 */
+#define TV_ALGO_AUTO 0    /* N <= 128: matrix-core path where it applies, else level-scheduled;
+                             N > 128: blocked */
+#define TV_ALGO_LEVEL 1   /* level-scheduled forward substitution, fp32 FMA, any d; N <= 128 */
+#define TV_ALGO_MFMA 2    /* bf16 matrix cores + per-node path solve; bf16, d_k = d_v = 128,
+                             N <= 128 */
+#define TV_ALGO_BLOCKED 3 /* blocked solve over depth-sorted chunks of path entries: any tree
+                             up to TV_MAX_NODES, any depth, any d (matrix-core contraction for
+                             bf16 at d_k = d_v = 128) */
 
 /* host return codes */
 #define TV_OK 0
 #define TV_ERR_NULL (-1)     /* a required pointer is NULL */
-#define TV_ERR_DIMS (-2)     /* B, H or N <= 0, N > TV_MAX_NODES, or a size overflows */
+#define TV_ERR_DIMS (-2)     /* B, H or N <= 0, N > TV_MAX_NODES (128 for the snapshot
+                                baseline), or a size overflows */
 #define TV_ERR_HEAD_DIM (-3) /* d_k or d_v not in {16, 32, 64, 128} */
 #define TV_ERR_MODE (-4)     /* bad dtype or mode, or beta == NULL in GDN mode */
 #define TV_ERR_ALIAS (-5)    /* an output overlaps an input it may not overlap */
@@ -106,7 +113,8 @@ int tree_verify(int B, int H, int N, int dk, int dv, int dtype, int mode, const 
                 void* stream);
 
 /* tree_verify with an explicit solver choice (TV_ALGO_*); same outputs within
- * floating-point rounding.  Used by tests to exercise both solvers. */
+ * floating-point rounding.  TV_ERR_ALGO when the choice does not apply to the
+ * arguments.  Used by tests to exercise every solver on the same inputs. */
 int tree_verify_algo(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
                      const void* k, const void* v, const float* alpha, const float* beta,
                      const int32_t* parents, const float* S_root, void* o, float* U,
@@ -157,7 +165,7 @@ int tree_index(int B, int N, const int32_t* parents, int32_t* depth, uint64_t* a
  *
  * tree_verify_snapshot -- visits the nodes of each (sequence, head) in index
  * order, computes S_n from its parent's snapshot (S_root for parent -1) and
- * writes it to snapshots, then o_n = S_n^T q_n.
+ * writes it to snapshots, then o_n = S_n^T q_n.  N <= 128.
  *   q, k, v, alpha, beta, parents, S_root, o, status: as in tree_verify
  *   snapshots [B, H, N, dk, dv] f32 OUT (caller-allocated: B H N dk dv 4 bytes)
  * Bad parents are flagged in status and treated as -1.
@@ -191,8 +199,9 @@ int tree_commit_snapshot(int B, int H, int N, int dk, int dv, const float* snaps
  * reconstruction formula: that rebuild is the per-token factors of the path
  * applied to the old root state).  For bf16 at d_k = d_v = 128 a single kernel
  * reads S_in once, applies the accepted path's rank-len update in registers,
- * writes S_out and verifies the new tree against it; other shapes run the two
- * kernels above in stream order.  Outputs match the two calls within
+ * writes S_out and verifies the new tree against it when both trees have at
+ * most 128 nodes; other shapes and sizes run the two kernels above in stream
+ * order.  Outputs match the two calls within
  * floating-point rounding (S_out to ~2^-24 relative, as tree_commit).
  *
  *   N_prev, k_prev, alpha_prev, U_prev, parents_prev, accepted_prev,

@@ -78,7 +78,7 @@ def test_verify_null_pointers(lib):
         assert _verify(lib, nulls=(i,), B=0) == TV_ERR_NULL
 
 
-@pytest.mark.parametrize("B,H,N", [(0, 1, 4), (1, 0, 4), (1, 1, 0), (1, 1, 129), (-3, 1, 4),
+@pytest.mark.parametrize("B,H,N", [(0, 1, 4), (1, 0, 4), (1, 1, 0), (1, 1, 513), (-3, 1, 4),
                                    (1 << 30, 1 << 20, 128)])
 def test_verify_bad_dims(lib, B, H, N):
     assert _verify(lib, B=B, H=H, N=N) == TV_ERR_DIMS
@@ -100,13 +100,16 @@ def test_verify_bad_algo(lib):
     assert _verify(lib, algo=2, dtype=0, dk=128, dv=128) == TV_ERR_ALGO   # fp32 has no MFMA path
     assert _verify(lib, algo=2, dtype=1, dk=64, dv=64) == TV_ERR_ALGO     # d != 128
     assert _verify(lib, algo=-1) == TV_ERR_ALGO
+    # the register-path and level kernels take trees of at most 128 nodes
+    assert _verify(lib, algo=2, dtype=1, dk=128, dv=128, N=129) == TV_ERR_ALGO
+    assert _verify(lib, algo=1, N=129) == TV_ERR_ALGO
 
 
 def test_commit_checks(lib):
     P = FAKE
     assert lib.tree_commit(1, 1, 4, 16, 16, 0, None, P, P, P, P, P, P, None, None, None) == TV_ERR_NULL
     assert lib.tree_commit(1, 1, 4, 16, 16, 0, P, P, P, P, None, P, P, None, None, None) == TV_ERR_NULL
-    assert lib.tree_commit(1, 1, 200, 16, 16, 0, P, P, P, P, P, P, P, None, None, None) == TV_ERR_DIMS
+    assert lib.tree_commit(1, 1, 513, 16, 16, 0, P, P, P, P, P, P, P, None, None, None) == TV_ERR_DIMS
     assert lib.tree_commit(1, 1, 4, 16, 24, 0, P, P, P, P, P, P, P, None, None, None) == TV_ERR_HEAD_DIM
     assert lib.tree_commit(1, 1, 4, 16, 16, 5, P, P, P, P, P, P, P, None, None, None) == TV_ERR_MODE
     # S_out starting 4 bytes into S_root: partial overlap
@@ -121,7 +124,7 @@ def test_index_checks(lib):
     assert lib.tree_index(1, 4, None, P, P, None, None) == TV_ERR_NULL
     assert lib.tree_index(1, 4, P, None, P, None, None) == TV_ERR_NULL
     assert lib.tree_index(0, 4, P, P, P, None, None) == TV_ERR_DIMS
-    assert lib.tree_index(1, 129, P, P, P, None, None) == TV_ERR_DIMS
+    assert lib.tree_index(1, 513, P, P, P, None, None) == TV_ERR_DIMS
 
 
 def test_snapshot_checks(lib):
@@ -131,7 +134,7 @@ def test_snapshot_checks(lib):
     ptrs = [P] * 9 + [None]   # q k v alpha beta parents S_root snapshots o, status = NULL
     assert lib.tree_verify_snapshot(*args(), *([None] + ptrs[1:]), None) == TV_ERR_NULL
     assert lib.tree_verify_snapshot(*args(), *(ptrs[:7] + [None] + ptrs[8:]), None) == TV_ERR_NULL
-    assert lib.tree_verify_snapshot(*args(N=129), *ptrs, None) == TV_ERR_DIMS
+    assert lib.tree_verify_snapshot(*args(N=129), *ptrs, None) == TV_ERR_DIMS   # baseline: N <= 128
     assert lib.tree_verify_snapshot(*args(dv=48), *ptrs, None) == TV_ERR_HEAD_DIM
     assert lib.tree_verify_snapshot(*args(mode=3), *ptrs, None) == TV_ERR_MODE
     nob = ptrs[:4] + [None] + ptrs[5:]
@@ -141,6 +144,7 @@ def test_snapshot_checks(lib):
     assert lib.tree_commit_snapshot(1, 1, 4, 16, 16, None, P, P, P, None, None, None) == TV_ERR_NULL
     assert lib.tree_commit_snapshot(1, 1, 4, 16, 16, P, P, None, P, None, None, None) == TV_ERR_NULL
     assert lib.tree_commit_snapshot(1, 1, 0, 16, 16, P, P, P, P, None, None, None) == TV_ERR_DIMS
+    assert lib.tree_commit_snapshot(1, 1, 129, 16, 16, P, P, P, P, None, None, None) == TV_ERR_DIMS
     # S_out inside the snapshot buffer
     s0 = ctypes.c_void_p(0x100000)
     s1 = ctypes.c_void_p(0x100000 + 4 * 16 * 16)
@@ -160,8 +164,8 @@ def test_commit_verify_checks(lib):
         assert call(**{f"p{i}": None}) == TV_ERR_NULL, i
     assert call(p13=None, mode=0) == TV_ERR_MODE          # GDN needs beta
     assert call(Np=0) == TV_ERR_DIMS
-    assert call(Np=129) == TV_ERR_DIMS
-    assert call(N=129) == TV_ERR_DIMS
+    assert call(Np=513) == TV_ERR_DIMS
+    assert call(N=513) == TV_ERR_DIMS
     assert call(dv=48) == TV_ERR_HEAD_DIM
     assert call(dtype=3) == TV_ERR_MODE
     assert call(mode=4) == TV_ERR_MODE

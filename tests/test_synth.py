@@ -24,8 +24,8 @@ def test_deterministic(cfg):
 
 def test_shapes_and_trees():
     for cfg, spec in synth.CONFIGS.items():
-        if cfg == 5:
-            bt = synth.make_inputs(5, B=4, H=2)
+        if cfg >= 5:
+            bt = synth.make_inputs(cfg, B=4, H=2)
             B, H = 4, 2
         else:
             bt = synth.make_inputs(cfg)
@@ -54,6 +54,10 @@ def test_shapes_and_trees():
                 assert kids[0] == 16 and list(par[1:17]) == [0] * 16
                 assert dep.max() <= 10 and kids[1:].max() <= 8
                 assert kids[a] == 0   # a leaf
+            if cfg == 6:
+                assert kids[0] == 32 and list(par[1:33]) == [0] * 32
+                assert dep.max() <= 12 and kids[1:].max() <= 8
+                assert kids[a] == 0
         if spec["dtype"] == synth.BF16:
             for x in (bt.q, bt.k, bt.v):
                 assert not np.any(x.view(np.uint32) & 0xFFFF)

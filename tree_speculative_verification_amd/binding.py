@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
 
 TV_F32, TV_BF16 = 0, 1
 TV_GDN, TV_SCALAR_DECAY = 0, 1
-TV_ALGO_AUTO, TV_ALGO_LEVEL, TV_ALGO_MFMA = 0, 1, 2
-TV_MAX_NODES = 128
+TV_ALGO_AUTO, TV_ALGO_LEVEL, TV_ALGO_MFMA, TV_ALGO_BLOCKED = 0, 1, 2, 3
+TV_MAX_NODES = 512
+TV_MAX_NODES_SNAPSHOT = 128
 
 SYMBOLS = ["tree_verify", "tree_verify_algo", "tree_commit", "tree_index", "tree_verify_snapshot",
            "tree_commit_snapshot", "tree_commit_verify", "tv_status_string", "tv_version"]

@@ -23,7 +23,8 @@ LIB = os.path.join(PKG, "libtreeverify.so")
 ARCH = "gfx950"
 
 SOURCES = ["tv_api.cpp", "tv_commit.hip", "tv_verify_level.hip", "tv_verify_mfma.hip",
-           "tv_snapshot.hip"]
+           "tv_snapshot.hip",
+           "tv_verify_blocked.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

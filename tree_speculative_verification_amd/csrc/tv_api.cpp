@@ -26,6 +26,35 @@ bool snapshot_size_ok(long long B, long long H, long long N, long long dk, long 
 
 int hip_code(int err) { return err == 0 ? TV_OK : TV_ERR_HIP_BASE - err; }
 
+// Trees the register-path (matrix-core) and level-scheduled kernels take; the
+// blocked kernel takes every tree up to TV_MAX_NODES.
+constexpr int kSmallTree = 128;
+
+// Solver for tree_verify_algo's TV_ALGO_AUTO, or TV_ERR_ALGO for a choice that
+// does not apply to these arguments.
+int pick_algo(int algo, int N, int dk, int dv, int dtype) {
+  const bool mfma_ok = dtype == TV_BF16 && dk == 128 && dv == 128 && N <= kSmallTree;
+  if (algo == TV_ALGO_AUTO) return N > kSmallTree ? TV_ALGO_BLOCKED : (mfma_ok ? TV_ALGO_MFMA : TV_ALGO_LEVEL);
+  if (algo == TV_ALGO_MFMA) return mfma_ok ? algo : TV_ERR_ALGO;
+  if (algo == TV_ALGO_LEVEL) return N <= kSmallTree ? algo : TV_ERR_ALGO;
+  if (algo == TV_ALGO_BLOCKED) return algo;
+  return TV_ERR_ALGO;
+}
+
+int launch_algo(int algo, int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                const void* k, const void* v, const float* alpha, const float* beta,
+                const int32_t* parents, const float* S_root, void* o, float* U, int32_t* status,
+                hipStream_t st) {
+  if (algo == TV_ALGO_MFMA)
+    return tv::launch_verify_mfma(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U,
+                                  status, st);
+  if (algo == TV_ALGO_BLOCKED)
+    return tv::launch_verify_blocked(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta, parents,
+                                     S_root, o, U, status, st);
+  return tv::launch_verify_level(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta, parents,
+                                 S_root, o, U, status, st);
+}
+
 int check_common(int B, int H, int N, int dk, int dv, int dtype) {
   if (B <= 0 || H <= 0 || N <= 0 || N > TV_MAX_NODES) return TV_ERR_DIMS;
   if (!head_dim_ok(dk) || !head_dim_ok(dv)) return TV_ERR_HEAD_DIM;
@@ -47,19 +76,10 @@ int tree_verify_algo(int B, int H, int N, int dk, int dv, int dtype, int mode, c
   if (rc) return rc;
   if (mode != TV_GDN && mode != TV_SCALAR_DECAY) return TV_ERR_MODE;
   if (mode == TV_GDN && !beta) return TV_ERR_MODE;
-  const bool mfma_ok = dtype == TV_BF16 && dk == 128 && dv == 128;
-  if (algo == TV_ALGO_AUTO) algo = mfma_ok ? TV_ALGO_MFMA : TV_ALGO_LEVEL;
-  if (algo == TV_ALGO_MFMA && !mfma_ok) return TV_ERR_ALGO;
-  if (algo != TV_ALGO_MFMA && algo != TV_ALGO_LEVEL) return TV_ERR_ALGO;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  int err;
-  if (algo == TV_ALGO_MFMA)
-    err = tv::launch_verify_mfma(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U,
-                                 status, st);
-  else
-    err = tv::launch_verify_level(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta, parents,
-                                  S_root, o, U, status, st);
-  return hip_code(err);
+  algo = pick_algo(algo, N, dk, dv, dtype);
+  if (algo < 0) return algo;
+  return hip_code(launch_algo(algo, B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta, parents,
+                              S_root, o, U, status, static_cast<hipStream_t>(stream)));
 }
 
 int tree_verify(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
@@ -100,7 +120,7 @@ int tree_verify_snapshot(int B, int H, int N, int dk, int dv, int dtype, int mod
   if (rc) return rc;
   if (mode != TV_GDN && mode != TV_SCALAR_DECAY) return TV_ERR_MODE;
   if (mode == TV_GDN && !beta) return TV_ERR_MODE;
-  if (!snapshot_size_ok(B, H, N, dk, dv)) return TV_ERR_DIMS;
+  if (N > kSmallTree || !snapshot_size_ok(B, H, N, dk, dv)) return TV_ERR_DIMS;
   return hip_code(tv::launch_snapshot_verify(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta,
                                              parents, S_root, snapshots, o, status,
                                              static_cast<hipStream_t>(stream)));
@@ -112,7 +132,7 @@ int tree_commit_snapshot(int B, int H, int N, int dk, int dv, const float* snaps
   if (!snapshots || !parents || !accepted || !S_out) return TV_ERR_NULL;
   int rc = check_common(B, H, N, dk, dv, TV_F32);
   if (rc) return rc;
-  if (!snapshot_size_ok(B, H, N, dk, dv)) return TV_ERR_DIMS;
+  if (N > kSmallTree || !snapshot_size_ok(B, H, N, dk, dv)) return TV_ERR_DIMS;
   const uintptr_t sb = reinterpret_cast<uintptr_t>(snapshots);
   const uintptr_t se = sb + (uintptr_t)B * H * N * dk * dv * sizeof(float);
   const uintptr_t ob = reinterpret_cast<uintptr_t>(S_out);
@@ -147,7 +167,7 @@ int tree_commit_verify(int B, int H, int N_prev, int N, int dk, int dv, int dtyp
   const uintptr_t unb = (uintptr_t)B * H * N * dv * sizeof(float);
   if (up < un + unb && un < up + upb) return TV_ERR_ALIAS;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == TV_BF16 && dk == 128 && dv == 128) {
+  if (dtype == TV_BF16 && dk == 128 && dv == 128 && N <= kSmallTree && N_prev <= kSmallTree) {
     tv::PrevCommit pc;
     pc.N = N_prev;
     pc.k = static_cast<const uint16_t*>(k_prev);
@@ -161,12 +181,12 @@ int tree_commit_verify(int B, int H, int N_prev, int N, int dk, int dv, int dtyp
     return hip_code(tv::launch_verify_mfma(B, H, N, mode, q, k, v, alpha, beta, parents, S_in, o, U,
                                            status, st, &pc));
   }
-  // other shapes: the two kernels in stream order
+  // other shapes and trees: the two kernels in stream order
   int err = tv::launch_commit(B, H, N_prev, dk, dv, dtype, k_prev, alpha_prev, U_prev, parents_prev,
                               accepted_prev, S_in, S_out, path_out, commit_status, st);
   if (err) return hip_code(err);
-  return hip_code(tv::launch_verify_level(B, H, N, dk, dv, dtype, mode, q, k, v, alpha, beta,
-                                          parents, S_out, o, U, status, st));
+  return hip_code(launch_algo(pick_algo(TV_ALGO_AUTO, N, dk, dv, dtype), B, H, N, dk, dv, dtype,
+                              mode, q, k, v, alpha, beta, parents, S_out, o, U, status, st));
 }
 
 const char* tv_status_string(int code) {
@@ -175,7 +195,7 @@ const char* tv_status_string(int code) {
     case TV_STATUS_BAD_PARENTS: return "status: a parent index is outside [-1, i-1]";
     case TV_STATUS_BAD_ACCEPTED: return "status: accepted node index is outside [0, N)";
     case TV_ERR_NULL: return "a required pointer is NULL";
-    case TV_ERR_DIMS: return "bad sizes: B, H, N must be positive, N <= 128, sizes must fit";
+    case TV_ERR_DIMS: return "bad sizes: B, H, N must be positive, N <= 512 (128 for the snapshot baseline), sizes must fit";
     case TV_ERR_HEAD_DIM: return "d_k and d_v must be 16, 32, 64 or 128";
     case TV_ERR_MODE: return "bad dtype or mode, or beta is NULL in gated-delta-rule mode";
     case TV_ERR_ALIAS: return "an output overlaps an input it may not overlap (S_out == S_root in place is allowed)";

@@ -40,6 +40,47 @@ __global__ __launch_bounds__(kThreads) void index_kernel(int N, const int32_t* _
   if (tid == 0 && status) status[b] = bad ? 1 : 0;
 }
 
+// Trees above 128 nodes: one thread per node walks its path and writes the
+// ancestor words as it crosses them (indices fall along the walk, so each word
+// is finished before the next lower one starts).
+__global__ __launch_bounds__(kMaxTree) void index_wide_kernel(int N,
+                                                             const int32_t* __restrict__ parents,
+                                                             int32_t* __restrict__ depth,
+                                                             unsigned long long* __restrict__ anc,
+                                                             int32_t* __restrict__ status) {
+  __shared__ int spar[kMaxTree];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int W = (N + 63) / 64;
+  int p = -1;
+  if (tid < N) {
+    p = parents[(size_t)b * N + tid];
+    spar[tid] = p;
+  }
+  const bool bad = __syncthreads_or(tid < N && (p < -1 || p >= tid)) != 0;
+  if (tid == 0 && status) status[b] = bad ? 1 : 0;
+  if (tid >= N) return;
+  unsigned long long* a = anc + ((size_t)b * N + tid) * W;
+  for (int w = 0; w < W; ++w) a[w] = 0ull;
+  if (bad) {
+    depth[(size_t)b * N + tid] = 0;
+    return;
+  }
+  int d = -1, w = tid >> 6;
+  unsigned long long bits = 0ull;
+  for (int j = tid; j >= 0; j = spar[j]) {
+    if ((j >> 6) != w) {
+      a[w] = bits;
+      w = j >> 6;
+      bits = 0ull;
+    }
+    bits |= 1ull << (j & 63);
+    ++d;
+  }
+  a[w] = bits;
+  depth[(size_t)b * N + tid] = d;
+}
+
 // One workgroup per (sequence, head, tile of RT = RPP * P state rows); with
 // P = DV / 8 a tile is 128 rows, i.e. the whole d_k x d_v state at d_k = 128.
 // Thread t owns float4 column group t % CG of rows r0 + t / CG + p * RPP.
@@ -61,10 +102,10 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   constexpr int CH = 16;                // path entries staged per round
   constexpr int VE = 16 / sizeof(TK);   // k elements per 16-byte load
   static_assert(RT % VE == 0, "tile rows come in whole 16-byte k chunks");
-  __shared__ int spar[kMaxNodes];
-  __shared__ float sal[kMaxNodes];
-  __shared__ int pidx[kMaxNodes];       // path, accepted node first (distance order)
-  __shared__ float coef[kMaxNodes];     // D(pidx[i] -> a): product of alpha over distances < i
+  __shared__ int spar[kMaxTree];
+  __shared__ float sal[kMaxTree];
+  __shared__ int pidx[kMaxTree];        // path, accepted node first (distance order)
+  __shared__ float coef[kMaxTree];      // D(pidx[i] -> a): product of alpha over distances < i
   __shared__ float gam;
   __shared__ int slen;
   __shared__ float4 ush[CH][CG];
@@ -84,6 +125,15 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   const int pn = tid < N ? tid : N - 1;
   const int par_v = parents[(size_t)b * N + pn];
   const float a_all = alpha[(size_t)(b * N + pn) * H + h];
+  // trees above kThreads nodes: a second node per thread
+  const int tid2 = tid + kThreads;
+  int par_v2 = -1;
+  float a_all2 = 1.f;
+  if (N > kThreads) {
+    const int pn2 = tid2 < N ? tid2 : N - 1;
+    par_v2 = parents[(size_t)b * N + pn2];
+    a_all2 = alpha[(size_t)(b * N + pn2) * H + h];
+  }
   const int a_in = accepted[b];
   const float4* Sp = reinterpret_cast<const float4*>(S_root + (size_t)bh * dk * DV);
   float4 acc[P];
@@ -96,7 +146,12 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
     spar[tid] = par_v;
     sal[tid] = a_all;
   }
-  const bool bad_par = __syncthreads_or(tid < N && (par_v < -1 || par_v >= tid)) != 0;
+  if (tid2 < N) {
+    spar[tid2] = par_v2;
+    sal[tid2] = a_all2;
+  }
+  const bool bad_par = __syncthreads_or((tid < N && (par_v < -1 || par_v >= tid)) ||
+                                        (tid2 < N && (par_v2 < -1 || par_v2 >= tid2))) != 0;
   const bool bad_acc = a_in < 0 || a_in >= N;
   if (tid == 0) {
     // walk up from the accepted node; parents[i] < i makes it end within N steps
@@ -117,8 +172,9 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   const int L = slen;
   if (h == 0 && tile == 0) {
     if (tid == 0 && status) status[b] = bad_par ? 1 : (bad_acc ? 2 : 0);
-    if (path_out && tid < N)
-      path_out[(size_t)b * N + tid] = (!bad_par && !bad_acc && tid < L) ? pidx[L - 1 - tid] : -1;
+    if (path_out)
+      for (int i = tid; i < N; i += kThreads)
+        path_out[(size_t)b * N + i] = (!bad_par && !bad_acc && i < L) ? pidx[L - 1 - i] : -1;
   }
   const float g = gam;
 #pragma unroll
@@ -182,8 +238,12 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
 
 int launch_index(int B, int N, const int32_t* parents, int32_t* depth, uint64_t* anc,
                  int32_t* status, hipStream_t stream) {
-  hipLaunchKernelGGL(index_kernel, dim3(B), dim3(kThreads), 0, stream, N, parents, depth,
-                     reinterpret_cast<unsigned long long*>(anc), status);
+  if (N > kMaxNodes)
+    hipLaunchKernelGGL(index_wide_kernel, dim3(B), dim3(kMaxTree), 0, stream, N, parents, depth,
+                       reinterpret_cast<unsigned long long*>(anc), status);
+  else
+    hipLaunchKernelGGL(index_kernel, dim3(B), dim3(kThreads), 0, stream, N, parents, depth,
+                       reinterpret_cast<unsigned long long*>(anc), status);
   return static_cast<int>(hipGetLastError());
 }
 

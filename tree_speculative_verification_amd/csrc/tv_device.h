@@ -13,7 +13,8 @@
 
 namespace tv {
 
-constexpr int kMaxNodes = 128;
+constexpr int kMaxNodes = 128;   // trees the register-path and level kernels take
+constexpr int kMaxTree = 512;    // trees the blocked kernel, commit and index take
 constexpr int kThreads = 256;
 constexpr int kGdn = 0;
 constexpr int kScalar = 1;

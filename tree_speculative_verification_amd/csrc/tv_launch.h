@@ -20,6 +20,12 @@ int launch_verify_level(int B, int H, int N, int dk, int dv, int dtype, int mode
                         const int32_t* parents, const float* S_root, void* o, float* U,
                         int32_t* status, hipStream_t stream);
 
+// Blocked solve for trees of up to 512 nodes and any depth (tv_verify_blocked.hip).
+int launch_verify_blocked(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
+                          const void* k, const void* v, const float* alpha, const float* beta,
+                          const int32_t* parents, const float* S_root, void* o, float* U,
+                          int32_t* status, hipStream_t stream);
+
 // The previous step's commit, applied to the state on the fly by the fused
 // verification (arrays as tree_commit takes them, N = the previous tree's size).
 struct PrevCommit {

@@ -4,9 +4,10 @@ This module only draws inputs: tree shapes, accepted nodes, q/k/v, gates and the
 root state. It holds none of the verification arithmetic, so the GPU path, the
 fp64 checker and the benchmark can all take their inputs from it.
 
-The five workloads follow the shapes that the Twig/Bole and TreeWY pages talk
+The workloads follow the shapes that the Twig/Bole and TreeWY pages talk
 about (hybrid models whose linear-attention layers carry a d_k x d_v state,
-draft trees of a few dozen to ~128 nodes, batch-wide verification):
+draft trees of a few dozen to ~128 nodes, batch-wide verification), plus one
+wider tree of the kind the pages say the method makes affordable:
 
   1  gated delta rule, fp32, B=1 H=1 d=16, the 7-node tree [-1,0,0,1,1,2,3], accepted 6
   2  scalar decay (S = lam*S + k v^T, the page-4 closed form), fp32, B=4 H=8 d=64,
@@ -16,6 +17,8 @@ draft trees of a few dozen to ~128 nodes, batch-wide verification):
      (depth <= 8, <= 4 children), accepted uniform over nodes
   5  gated delta rule, bf16 q/k/v, B=128 H=64 d=128, 128-node wide tree
      (root fan-out 16, depth <= 10, <= 8 children), accepted uniform over leaves
+  6  gated delta rule, bf16 q/k/v, B=16 H=32 d=128, 512-node wide tree
+     (root fan-out 32, depth <= 12, <= 8 children), accepted uniform over leaves
 
 Draw order per call is fixed: trees, accepted, q, k, v, alpha (or its log), beta,
 S_root, all from one numpy PCG64 generator.  bf16 values are produced by
@@ -98,6 +101,7 @@ CONFIGS = {
     3: dict(mode=GDN, dtype=BF16, B=8, H=32, N=8, d=128),
     4: dict(mode=GDN, dtype=BF16, B=32, H=32, N=64, d=128),
     5: dict(mode=GDN, dtype=BF16, B=128, H=64, N=128, d=128),
+    6: dict(mode=GDN, dtype=BF16, B=16, H=32, N=512, d=128),
 }
 
 CONFIG_NAMES = {
@@ -106,6 +110,7 @@ CONFIG_NAMES = {
     3: "gdn-bf16 B8 H32 N8 d128 chain",
     4: "gdn-bf16 B32 H32 N64 d128 random tree depth<=8 fanout<=4",
     5: "gdn-bf16 B128 H64 N128 d128 wide tree rootfan16 depth<=10 fanout<=8",
+    6: "gdn-bf16 B16 H32 N512 d128 wide tree rootfan32 depth<=12 fanout<=8",
 }
 
 
@@ -172,7 +177,7 @@ def _normal(rng, shape, dtype):
 
 def make_inputs(cfg: int, seed: Optional[int] = None, B: Optional[int] = None,
                 H: Optional[int] = None) -> TreeBatch:
-    """Inputs of workload `cfg` (1..5); `seed` defaults to the workload number.
+    """Inputs of workload `cfg` (1..6); `seed` defaults to the workload number.
 
     B and H may be reduced (the per-sequence draws keep their order, so a
     smaller B gives the first sequences of a bigger one only for the trees and
@@ -193,9 +198,12 @@ def make_inputs(cfg: int, seed: Optional[int] = None, B: Optional[int] = None,
         parents = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
     elif cfg == 4:
         parents = np.stack([random_tree(rng, N, max_depth=8, max_children=4) for _ in range(B)])
-    else:
+    elif cfg == 5:
         parents = np.stack([random_tree(rng, N, max_depth=10, max_children=8, first_parent=1,
                                         fixed_root_children=16) for _ in range(B)])
+    else:
+        parents = np.stack([random_tree(rng, N, max_depth=12, max_children=8, first_parent=1,
+                                        fixed_root_children=32) for _ in range(B)])
     parents = parents.astype(np.int32)
 
     # accepted nodes
