@@ -22,7 +22,10 @@ of the fused pipeline.  Per-kernel durations for the roofline come from K
 back-to-back launches of each kernel over the same ring.
 
 Prints ONE JSON line.  Options: --steps K --warmup W --gpus 1 (only 1 is
-supported: the path runs on one GPU) --workload {3,4,5} --no-cpu-baseline.
+supported: the path runs on one GPU) --workload {3,4,5,6} --no-cpu-baseline.
+Workload 6 (512-node trees) runs the blocked verification kernel; its step is
+tree_commit_verify's two launches (commit, then blocked verify), and the
+roofline line reports the blocked verify kernel.
 """
 from __future__ import annotations
 
@@ -42,14 +45,19 @@ from tree_speculative_verification_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified tree nodes/s per GDN layer (1 GPU) + % of HBM roofline"
+_CSRC = "tree_speculative_verification_amd/csrc/"
 KERNEL_SOURCES = {
-    "verify": ["tree_speculative_verification_amd/csrc/tv_verify_mfma.hip",
-               "tree_speculative_verification_amd/csrc/tv_device.h"],
-    "fused": ["tree_speculative_verification_amd/csrc/tv_verify_mfma.hip",
-              "tree_speculative_verification_amd/csrc/tv_device.h"],
-    "commit": ["tree_speculative_verification_amd/csrc/tv_commit.hip",
-               "tree_speculative_verification_amd/csrc/tv_device.h"],
+    "verify": [_CSRC + "tv_verify_mfma.hip", _CSRC + "tv_device.h"],
+    "fused": [_CSRC + "tv_verify_mfma.hip", _CSRC + "tv_device.h"],
+    "commit": [_CSRC + "tv_commit.hip", _CSRC + "tv_device.h"],
 }
+# trees above 128 nodes: blocked verification, and commit + blocked verify as the step
+KERNEL_SOURCES_LARGE = {
+    "verify": [_CSRC + "tv_verify_blocked.hip", _CSRC + "tv_device.h"],
+    "fused": [_CSRC + "tv_verify_blocked.hip", _CSRC + "tv_commit.hip", _CSRC + "tv_device.h"],
+    "commit": [_CSRC + "tv_commit.hip", _CSRC + "tv_device.h"],
+}
+SMALL_TREE = 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -78,9 +86,9 @@ def algorithmic_bytes(bt):
     return int(verify), int(commit), int(fused), L
 
 
-def sources_sha(kind):
+def sources_sha(kind, large=False):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kind]:
+    for rel in (KERNEL_SOURCES_LARGE if large else KERNEL_SOURCES)[kind]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -94,7 +102,8 @@ def measured_traffic(kind, workload):
     except (OSError, ValueError):
         return None
     r = rec.get(f"{kind}_w{workload}")
-    if not r or r.get("source_sha") != sources_sha(kind):
+    large = synth.CONFIGS[workload]["N"] > SMALL_TREE
+    if not r or r.get("source_sha") != sources_sha(kind, large):
         return None
     return r.get("bytes_per_launch")
 
@@ -211,7 +220,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5])
+    ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--cpu-reps", type=int, default=3,
@@ -310,7 +319,8 @@ def main(argv=None):
 
     base = None
     snap_bytes = B * H * N * dk * dv * 4
-    if not a.no_snapshot_baseline and snap_bytes <= (64 << 30):
+    large = N > SMALL_TREE
+    if not a.no_snapshot_baseline and snap_bytes <= (64 << 30) and not large:
         base = snapshot_baseline(tvb, sets, R, bt, stream, timed, a.steps, ms_step, snap_bytes)
 
     value = B * N / (ms_step * 1e-3)
@@ -322,8 +332,14 @@ def main(argv=None):
         kern[name] = {"mean_us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
                       "frac": round(gbs / HBM_PEAK_GBS, 4),
                       "traffic": measured_traffic(name, a.workload)}
-    kern["fused"]["entry"] = "tree_commit_verify (one launch per step)"
-    dom = "fused"
+    if large:
+        kern["fused"]["entry"] = ("tree_commit_verify (trees above 128 nodes: commit, then the "
+                                  "blocked verification, two launches per step)")
+        kern["verify"]["kernel"] = "blocked verification (verify_blocked_kernel)"
+        dom = "verify"
+    else:
+        kern["fused"]["entry"] = "tree_commit_verify (one launch per step)"
+        dom = "fused"
     combined_gbs = (vbytes + cbytes) / (ms_two * 1e-3) / 1e9
     snap = B * H * N * dk * dv * 4
     u_only = B * H * N * dv * 4
@@ -336,8 +352,11 @@ def main(argv=None):
         "config": {"workload": synth.CONFIG_NAMES[a.workload], "B": B, "H": H, "N": N,
                    "d_k": dk, "d_v": dv, "qkv": "bf16", "state": "fp32", "layer": "gated delta rule",
                    "mean_path_len": round(float(L.mean()), 3),
-                   "pipeline": "fused: one tree_commit_verify launch per step (commit of the "
-                               "batch verified 2 steps earlier + verify of this batch)",
+                   "pipeline": ("tree_commit_verify per step: commit of the batch verified 2 "
+                                "steps earlier, then the blocked verification of this batch"
+                                if large else
+                                "fused: one tree_commit_verify launch per step (commit of the "
+                                "batch verified 2 steps earlier + verify of this batch)"),
                    "timing": f"HIP events around K steps on the launch stream; ring of {R} input "
                              "copies (>= 1 GB) so every kernel reads cold data; commit lags verify "
                              "by 2 steps"},
@@ -357,7 +376,9 @@ def main(argv=None):
                                   "ratio_snapshots_to_U": round(snap / u_only, 2),
                                   "ratio_snapshots_to_U_K_gates": round(snap / u_k_g, 2)},
         "cpu_baseline": cpu,
-        "snapshot_baseline": base,
+        "snapshot_baseline": base if not large else {
+            "skipped": "the per-node-snapshot kernels take trees of at most 128 nodes "
+                       f"(this batch would need {snap_bytes} bytes of snapshots)"},
     }
     print(json.dumps(out), flush=True)
     return 0

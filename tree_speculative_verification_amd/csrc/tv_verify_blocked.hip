@@ -27,13 +27,18 @@
 // value columns):
 //   1. tree index: pointer jumping gives each node's path length and gamma;
 //      nodes are then sorted by depth (counting sort) and given entry offsets;
-//   2. R and gamma QS for every node: on matrix cores for bf16 with
-//      d_k = d_v = 128 (32x32x16 bf16, S split into hi + lo words), else fp32
-//      FMA.  R goes to LDS; gamma QS is parked in the node's U row in HBM,
-//      which the output step reads back just before it stores u there;
+//   2. R and gamma QS for every node into LDS: on matrix cores for bf16 with
+//      d_k = d_v = 128 (32x32x16 bf16, S split into hi + lo words; the S block
+//      and the first node tile are loaded before step 1, so their HBM latency
+//      hides under the tree build), else fp32 FMA;
 //   3. per chunk: path walk (entry nodes and decays), Gram dot products by
-//      8-lane groups (the ancestor-masked Gram/decay builder), level solve,
-//      outputs.
+//      one 8-lane group per node, four of its entries in flight at a time
+//      (the ancestor-masked Gram/decay builder), level solve, outputs (U and
+//      o stored to HBM once).
+//
+// One workgroup fills most of a CU's LDS (R/U and gamma QS for 512 nodes x 32
+// columns are 128 KB), so a CU runs one at a time and latency is hidden inside
+// the workgroup: eight waves, loads issued ahead of use.
 #include "tv_device.h"
 #include "tv_launch.h"
 
@@ -41,9 +46,9 @@ namespace tv {
 
 namespace {
 
-constexpr int kBT = 512;    // threads per workgroup
+constexpr int kBT = 1024;   // threads per workgroup (16 waves: one node tile each)
 constexpr int kBVB = 32;    // value columns per workgroup (d_v when d_v < 32)
-constexpr int kBEnt = 2048; // path entries per chunk
+constexpr int kBEnt = 1400; // path entries per chunk (what LDS has room for)
 constexpr int kBD = 128;    // d_k = d_v of the matrix-core contraction
 
 typedef __bf16 bbf16x8 __attribute__((ext_vector_type(8)));
@@ -51,19 +56,19 @@ typedef __bf16 bbf16x2 __attribute__((ext_vector_type(2)));
 typedef float bf32x16 __attribute__((ext_vector_type(16)));
 
 struct BlockedLds {
-  float U[kMaxTree * kBVB];  // R rows, solved in place into U rows (row stride = columns)
-  float cA[kBEnt];           // decay during the walk, then beta_n D (k_n.k_j)
-  float cP[kBEnt];           // D (q_n.k_j)
-  uint16_t en[kBEnt];        // the entry's path node j
-  uint16_t eo[kBEnt];        // the entry's own node n
-  int par[kMaxTree];
-  int jmp[kMaxTree];
-  int len[kMaxTree];         // path length = depth + 1
-  int ord[kMaxTree];         // position -> node, positions sorted by depth
-  int off[kMaxTree + 1];     // position -> first entry; off[N] = all entries
-  int lst[kMaxTree + 1];     // depth -> first position
-  int ebase[kMaxTree + 1];   // depth -> first entry
-  int hist[kMaxTree];        // nodes per depth
+  float U[kMaxTree * kBVB];   // R rows, solved in place into U rows (row stride = columns)
+  float QS[kMaxTree * kBVB];  // gamma_n QS_n rows
+  float cA[kBEnt];            // decay during the walk, then beta_n D (k_n.k_j)
+  float cP[kBEnt];            // D (q_n.k_j)
+  uint16_t en[kBEnt];         // the entry's path node j
+  int16_t par[kMaxTree];
+  int16_t jmp[kMaxTree];
+  int16_t len[kMaxTree];      // path length = depth + 1
+  int16_t ord[kMaxTree];      // position -> node, positions sorted by depth
+  int off[kMaxTree + 1];      // position -> first entry; off[N] = all entries
+  int lst[kMaxTree + 1];      // depth -> first position
+  int ebase[kMaxTree + 1];    // depth -> first entry
+  int hist[kMaxTree];         // nodes per depth
   float alp[kMaxTree];
   float bet[kMaxTree];
   float gam[kMaxTree];
@@ -103,87 +108,99 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return r;
 }
 
-// R (LDS) and gamma QS (parked in U, HBM) for node tiles on matrix cores.
-// A = S block^T (value column x d_k), B = [K or Q]^T (d_k x node): the
-// accumulator puts node lane%32 and value columns 8 (r/4) + 4 (lane/32) + r%4
-// in lane `lane`.
-__device__ void contract_mfma(BlockedLds& s, int N, int H, int b, int h, int bh, int c0, bool gdn,
-                              const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                              const uint16_t* __restrict__ v, const float* __restrict__ S_root,
-                              float* __restrict__ U) {
+// LDS rows of R/U and gamma QS: float4 column group g of node n is stored at
+// slot g ^ (n mod groups), so the lanes of a matrix-core tile (32 nodes, one
+// group) and of the solve (8 nodes x 8 groups) spread over all banks.
+__device__ __forceinline__ int urow(int n, int col, int vb) {
+  return n * vb + ((((col >> 2) ^ n) & ((vb >> 2) - 1)) << 2);
+}
+
+// Operands of one 32-node tile for the matrix-core contraction: q and k rows
+// (lane: node lane%32, 8 bf16 of each 16-wide d_k step) and v at the columns
+// the accumulator lands on.
+struct TileIn {
+  bbf16x8 qb[8], kb[8];
+  uint2 vv[4];
+};
+
+__device__ __forceinline__ void load_tile(TileIn& t, int T, int N, int H, int b, int h, int c0,
+                                          bool gdn, const uint16_t* __restrict__ q,
+                                          const uint16_t* __restrict__ k,
+                                          const uint16_t* __restrict__ v) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int lm = lane & 31, hi = lane >> 5;
-  // this lane's operand of S: rows 16 ks + 8 hi + i, column c0 + lm
-  bbf16x8 shi[8], slo[8];
-  {
-    const float* Sp = S_root + (size_t)bh * kBD * kBD + c0 + lm;
+  const int n = T * 32 + lm;
+  const size_t row = ((size_t)b * N + (n < N ? n : N - 1)) * H + h;
+  const uint16_t* qr = q + row * kBD + 8 * hi;
+  const uint16_t* kr = k + row * kBD + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      float x[8];
+  for (int ks = 0; ks < 8; ++ks) {
+    t.qb[ks] = *reinterpret_cast<const bbf16x8*>(qr + 16 * ks);
+    if (gdn) t.kb[ks] = *reinterpret_cast<const bbf16x8*>(kr + 16 * ks);
+  }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = Sp[(size_t)(16 * ks + 8 * hi + i) * kBD];
-      uint32_t wh[4], wl[4];
+  for (int g = 0; g < 4; ++g)
+    t.vv[g] = *reinterpret_cast<const uint2*>(v + row * kBD + c0 + 8 * g + 4 * hi);
+}
+
+// [K;Q] S_block products of one tile.  A = S block^T (value column x d_k),
+// taken from the S block staged in LDS (row-major, 32 columns) and split into
+// bf16 hi + lo words per 16-row step; B = [K or Q]^T (d_k x node).
+__device__ __forceinline__ void mma_tile(const TileIn& t, const float* Sst, bool gdn,
+                                         bf32x16& kacc, bf32x16& qacc) {
+  const int lane = threadIdx.x & 63;
+  const float* Sl = Sst + 8 * (lane >> 5) * kBVB + (lane & 31);  // rows 16 ks + 8 (lane/32) + i
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wh[i] = pack2_bf16(x[2 * i], x[2 * i + 1]);
-        const float h0 = __uint_as_float(wh[i] << 16), h1 = __uint_as_float(wh[i] & 0xffff0000u);
-        wl[i] = pack2_bf16(x[2 * i] - h0, x[2 * i + 1] - h1);
-      }
-      __builtin_memcpy(&shi[ks], wh, 16);
-      __builtin_memcpy(&slo[ks], wl, 16);
+  for (int r = 0; r < 16; ++r) {
+    kacc[r] = 0.f;
+    qacc[r] = 0.f;
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    uint32_t wh[4], wl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = Sl[(16 * ks + 2 * i) * kBVB], x1 = Sl[(16 * ks + 2 * i + 1) * kBVB];
+      wh[i] = pack2_bf16(x0, x1);
+      wl[i] = pack2_bf16(x0 - __uint_as_float(wh[i] << 16), x1 - __uint_as_float(wh[i] & 0xffff0000u));
+    }
+    bbf16x8 shi, slo;
+    __builtin_memcpy(&shi, wh, 16);
+    __builtin_memcpy(&slo, wl, 16);
+    qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, t.qb[ks], qacc, 0, 0, 0);
+    qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, t.qb[ks], qacc, 0, 0, 0);
+    if (gdn) {
+      kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, t.kb[ks], kacc, 0, 0, 0);
+      kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, t.kb[ks], kacc, 0, 0, 0);
     }
   }
-  const int ntiles = (N + 31) / 32;
-  for (int T = wave; T < ntiles; T += kBT / 64) {
-    const int n = T * 32 + lm;
-    const int nr = n < N ? n : N - 1;
-    const size_t row = ((size_t)b * N + nr) * H + h;
-    const uint16_t* kr = k + row * kBD + 8 * hi;
-    const uint16_t* qr = q + row * kBD + 8 * hi;
-    uint2 vv[4];
+}
+
+// R and gamma QS of one tile into LDS: the accumulator puts node lane%32 and
+// value columns 8 (r/4) + 4 (lane/32) + r%4 in lane `lane`.
+__device__ __forceinline__ void store_tile(BlockedLds& s, const TileIn& t, int T, int N, bool gdn,
+                                           const bf32x16& kacc, const bf32x16& qacc) {
+  const int lane = threadIdx.x & 63;
+  const int n = T * 32 + (lane & 31);
+  if (n >= N) return;
+  const float gn = s.gam[n], bn = s.bet[n];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      vv[g] = *reinterpret_cast<const uint2*>(v + row * kBD + c0 + 8 * g + 4 * hi);
-    bf32x16 kacc, qacc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      kacc[r] = 0.f;
-      qacc[r] = 0.f;
+  for (int g = 0; g < 4; ++g) {
+    const uint2 w = t.vv[g];
+    const float4 vf = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+    float4 r = vf;
+    if (gdn) {
+      r.x = bn * (vf.x - gn * kacc[4 * g + 0]);
+      r.y = bn * (vf.y - gn * kacc[4 * g + 1]);
+      r.z = bn * (vf.z - gn * kacc[4 * g + 2]);
+      r.w = bn * (vf.w - gn * kacc[4 * g + 3]);
     }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bbf16x8 qb = *reinterpret_cast<const bbf16x8*>(qr + 16 * ks);
-      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi[ks], qb, qacc, 0, 0, 0);
-      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo[ks], qb, qacc, 0, 0, 0);
-      if (gdn) {
-        const bbf16x8 kb = *reinterpret_cast<const bbf16x8*>(kr + 16 * ks);
-        kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi[ks], kb, kacc, 0, 0, 0);
-        kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo[ks], kb, kacc, 0, 0, 0);
-      }
-    }
-    if (n < N) {
-      const float gn = s.gam[n], bn = s.bet[n];
-      float* Ug = U + ((size_t)bh * N + n) * kBD + c0;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint2 w = vv[g];
-        const float4 vf = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                                      __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
-        float4 r = vf;
-        if (gdn) {
-          r.x = bn * (vf.x - gn * kacc[4 * g + 0]);
-          r.y = bn * (vf.y - gn * kacc[4 * g + 1]);
-          r.z = bn * (vf.z - gn * kacc[4 * g + 2]);
-          r.w = bn * (vf.w - gn * kacc[4 * g + 3]);
-        }
-        const int col = 8 * g + 4 * hi;
-        *reinterpret_cast<float4*>(&s.U[n * kBVB + col]) = r;
-        *reinterpret_cast<float4*>(Ug + col) =
-            make_float4(gn * qacc[4 * g + 0], gn * qacc[4 * g + 1], gn * qacc[4 * g + 2],
-                        gn * qacc[4 * g + 3]);
-      }
-    }
+    const int col = 8 * g + 4 * (lane >> 5);
+    *reinterpret_cast<float4*>(&s.U[urow(n, col, kBVB)]) = r;
+    *reinterpret_cast<float4*>(&s.QS[urow(n, col, kBVB)]) =
+        make_float4(gn * qacc[4 * g + 0], gn * qacc[4 * g + 1], gn * qacc[4 * g + 2],
+                    gn * qacc[4 * g + 3]);
   }
 }
 
@@ -192,7 +209,7 @@ template <typename TIn>
 __device__ void contract_fma(BlockedLds& s, int N, int H, int dk, int dv, int vb, int b, int h,
                              int bh, int c0, bool gdn, const TIn* __restrict__ q,
                              const TIn* __restrict__ k, const TIn* __restrict__ v,
-                             const float* __restrict__ S_root, float* __restrict__ U) {
+                             const float* __restrict__ S_root) {
   const int ncg = vb / 4;
   const float* Sb = S_root + (size_t)bh * dk * dv;
   for (int it = threadIdx.x; it < N * ncg; it += kBT) {
@@ -208,8 +225,8 @@ __device__ void contract_fma(BlockedLds& s, int N, int H, int dk, int dv, int vb
     const float gn = s.gam[n];
     float4 r = Elem<TIn>::load4(v, row * dv + c0 + col);
     if (gdn) r = mul4(s.bet[n], sub4(r, mul4(gn, ks)));
-    *reinterpret_cast<float4*>(&s.U[n * vb + col]) = r;
-    *reinterpret_cast<float4*>(U + ((size_t)bh * N + n) * dv + c0 + col) = mul4(gn, qs);
+    *reinterpret_cast<float4*>(&s.U[urow(n, col, vb)]) = r;
+    *reinterpret_cast<float4*>(&s.QS[urow(n, col, vb)]) = mul4(gn, qs);
   }
 }
 
@@ -221,6 +238,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     float* __restrict__ U, int32_t* __restrict__ status) {
   __shared__ BlockedLds s;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
   const int vb = dv < kBVB ? dv : kBVB;
   const int nvb = dv / vb;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -230,22 +248,41 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
   const int b = bh / H;
   const int c0 = cb * vb;
   const bool gdn = mode == kGdn;
+  const int ntiles = (N + 31) / 32;
+
+  // small loads first (loads return in order): parents and gates
+  const int pn = tid < N ? tid : N - 1;
+  int p_in = parents[(size_t)b * N + pn];
+  const float a_in = alpha[((size_t)b * N + pn) * H + h];
+  const float b_in = gdn ? beta[((size_t)b * N + pn) * H + h] : 0.f;
+
+  // matrix-core path: the S block (128 x 32 fp32, 16 KB) staged once in LDS by
+  // coalesced loads (in the U rows, unused until the contraction's results),
+  // and the wave's first node tile, both in flight during the tree build
+  TileIn t0;
+  if constexpr (MFMA) {
+    float4* Sl = reinterpret_cast<float4*>(s.U);
+    const float* Sb = S_root + (size_t)bh * kBD * kBD + c0;
+    static_assert(kBT * 4 == kBD * kBVB, "one float4 of the S block per thread");
+    Sl[tid] = *reinterpret_cast<const float4*>(Sb + (size_t)(tid >> 3) * kBD + 4 * (tid & 7));
+    if (wave < ntiles)
+      load_tile(t0, wave, N, H, b, h, c0, gdn, reinterpret_cast<const uint16_t*>(q),
+                reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v));
+  }
 
   // ---- 1. tree index ----
   if (tid == 0) s.maxd = 0;
   bool my_bad = false;
   if (tid < N) {
     s.hist[tid] = 0;
-    int p = parents[(size_t)b * N + tid];
-    const float a = alpha[((size_t)b * N + tid) * H + h];
-    s.alp[tid] = a;
-    s.bet[tid] = gdn ? beta[((size_t)b * N + tid) * H + h] : 0.f;
-    my_bad = p < -1 || p >= tid;
-    if (my_bad) p = -1;  // a parent outside [-1, i-1] is treated as -1 and flagged
-    s.par[tid] = p;
-    s.jmp[tid] = p;
+    my_bad = p_in < -1 || p_in >= tid;
+    if (my_bad) p_in = -1;  // a parent outside [-1, i-1] is treated as -1 and flagged
+    s.alp[tid] = a_in;
+    s.bet[tid] = b_in;
+    s.par[tid] = static_cast<int16_t>(p_in);
+    s.jmp[tid] = static_cast<int16_t>(p_in);
     s.len[tid] = 1;
-    s.gam[tid] = a;
+    s.gam[tid] = a_in;
   }
   const bool bad = __syncthreads_or(my_bad) != 0;
   // pointer jumping: a node's span (path nodes from it up to, not including,
@@ -263,8 +300,8 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     }
     if (!__syncthreads_or(j >= 0)) break;
     if (j >= 0) {
-      s.jmp[tid] = nj;
-      s.len[tid] += nl;
+      s.jmp[tid] = static_cast<int16_t>(nj);
+      s.len[tid] = static_cast<int16_t>(s.len[tid] + nl);
       s.gam[tid] *= ng;
     }
     __syncthreads();
@@ -291,7 +328,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
   __syncthreads();
   if (tid < N) {
     const int pos = s.lst[my_d] + atomicSub(&s.hist[my_d], 1) - 1;
-    s.ord[pos] = tid;
+    s.ord[pos] = static_cast<int16_t>(tid);
     s.off[pos] = s.ebase[my_d] + (pos - s.lst[my_d]) * (my_d + 1);
   }
   if (tid == 0) s.off[N] = s.ebase[maxd + 1];
@@ -300,15 +337,22 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
 
   // ---- 2. R and gamma QS ----
   if constexpr (MFMA) {
-    contract_mfma(s, N, H, b, h, bh, c0, gdn, q, k, v, S_root, U);
+    // one node tile per wave (N <= 512 is at most 16 tiles); the S block sits
+    // in the U rows until every wave has its products
+    static_assert(kMaxTree / 32 <= kBT / 64, "a node tile per wave");
+    bf32x16 kacc, qacc;
+    if (wave < ntiles) mma_tile(t0, s.U, gdn, kacc, qacc);
+    __syncthreads();
+    if (wave < ntiles) store_tile(s, t0, wave, N, gdn, kacc, qacc);
   } else {
-    contract_fma<TIn>(s, N, H, dk, dv, vb, b, h, bh, c0, gdn, q, k, v, S_root, U);
+    contract_fma<TIn>(s, N, H, dk, dv, vb, b, h, bh, c0, gdn, q, k, v, S_root);
   }
   __syncthreads();
 
   // ---- 3. chunks of path entries ----
   const int ncg = vb / 4;
   const int grp = tid >> 3, lj = tid & 7;
+  constexpr int kGroups = kBT / 8;
   for (int p0 = 0; p0 < N;) {
     const int e0 = s.off[p0];
     const int qpos = p0 + 1 + tid;
@@ -316,13 +360,12 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     const int nent = s.off[p1] - e0;
 
     // path walk: entry t of node n is (n, e_t) with decay D(e_t -> n)
-    if (p0 + tid < p1) {
-      const int n = s.ord[p0 + tid];
-      int x = s.off[p0 + tid] - e0;
+    for (int p = p0 + tid; p < p1; p += kBT) {
+      const int n = s.ord[p];
+      int x = s.off[p] - e0;
       float D = 1.f;
       for (int e = n; e >= 0; e = s.par[e]) {
         s.en[x] = static_cast<uint16_t>(e);
-        s.eo[x] = static_cast<uint16_t>(n);
         s.cA[x] = D;
         D *= s.alp[e];
         ++x;
@@ -330,37 +373,64 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     }
     __syncthreads();
 
-    // Gram values of the entries: one 8-lane group per entry
-    for (int x = grp; x < nent; x += kBT / 8) {
-      const int n = s.eo[x], e = s.en[x];
+    // Gram values of the entries: one 8-lane group per node (its q and k rows
+    // loaded once), its entries four at a time
+    for (int p = p0 + grp; p < p1; p += kGroups) {
+      const int n = s.ord[p];
+      const int x0 = s.off[p] - e0;
+      const int L = s.len[n];
+      const float bn = s.bet[n];
       const size_t rn = ((size_t)b * N + n) * H + h;
-      const size_t re = ((size_t)b * N + e) * H + h;
-      float kk = 0.f, qk = 0.f;
       if constexpr (MFMA) {
-        // bf16, d_k = 128: 16 elements per lane
-        const uint4* kn = reinterpret_cast<const uint4*>(k + rn * kBD) + 2 * lj;
+        // bf16, d_k = 128: lane lj covers elements [16 lj, 16 lj + 16)
         const uint4* qn = reinterpret_cast<const uint4*>(q + rn * kBD) + 2 * lj;
-        const uint4* ke = reinterpret_cast<const uint4*>(k + re * kBD) + 2 * lj;
-        const uint4 e0v = ke[0], e1v = ke[1];
-        qk = dot8_bf16(qn[0], e0v, qk);
-        qk = dot8_bf16(qn[1], e1v, qk);
+        const uint4* kn = reinterpret_cast<const uint4*>(k + rn * kBD) + 2 * lj;
+        const uint4 qa0 = qn[0], qa1 = qn[1];
+        uint4 ka0 = make_uint4(0, 0, 0, 0), ka1 = ka0;
         if (gdn) {
-          kk = dot8_bf16(kn[0], e0v, kk);
-          kk = dot8_bf16(kn[1], e1v, kk);
+          ka0 = kn[0];
+          ka1 = kn[1];
+        }
+        for (int t0 = 0; t0 < L; t0 += 4) {
+          uint4 ea[4][2];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = t0 + u < L ? s.en[x0 + t0 + u] : n;
+            const uint4* ke = reinterpret_cast<const uint4*>(k + (((size_t)b * N + e) * H + h) * kBD) + 2 * lj;
+            ea[u][0] = ke[0];
+            ea[u][1] = ke[1];
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float sq = dpp_sum8(dot8_bf16(qa1, ea[u][1], dot8_bf16(qa0, ea[u][0], 0.f)));
+            const float sk =
+                gdn ? dpp_sum8(dot8_bf16(ka1, ea[u][1], dot8_bf16(ka0, ea[u][0], 0.f))) : 0.f;
+            const int x = x0 + t0 + u;
+            if (lj == 0 && t0 + u < L) {
+              const float D = s.cA[x];
+              s.cP[x] = D * sq;
+              s.cA[x] = t0 + u > 0 ? bn * D * sk : 0.f;
+            }
+          }
         }
       } else {
-        for (int i = lj; i < dk; i += 8) {
-          const float ke = Elem<TIn>::load(k, re * dk + i);
-          qk = fmaf(Elem<TIn>::load(q, rn * dk + i), ke, qk);
-          if (gdn) kk = fmaf(Elem<TIn>::load(k, rn * dk + i), ke, kk);
+        for (int t = 0; t < L; ++t) {
+          const int e = s.en[x0 + t];
+          const size_t re = ((size_t)b * N + e) * H + h;
+          float a = 0.f, c = 0.f;
+          for (int i = lj; i < dk; i += 8) {
+            const float ke = Elem<TIn>::load(k, re * dk + i);
+            a = fmaf(Elem<TIn>::load(q, rn * dk + i), ke, a);
+            if (gdn) c = fmaf(Elem<TIn>::load(k, rn * dk + i), ke, c);
+          }
+          const float sq = dpp_sum8(a);
+          const float sk = dpp_sum8(c);
+          if (lj == 0) {
+            const float D = s.cA[x0 + t];
+            s.cP[x0 + t] = D * sq;
+            s.cA[x0 + t] = t > 0 ? bn * D * sk : 0.f;
+          }
         }
-      }
-      qk = dpp_sum8(qk);
-      kk = dpp_sum8(kk);
-      if (lj == 0) {
-        const float D = s.cA[x];
-        s.cP[x] = D * qk;
-        s.cA[x] = e != n ? s.bet[n] * D * kk : 0.f;
       }
     }
     __syncthreads();
@@ -377,37 +447,39 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
           const int col = 4 * (it % ncg);
           const int n = s.ord[p];
           const int x = s.off[p] - e0;
-          float4 u = *reinterpret_cast<const float4*>(&s.U[n * vb + col]);
+          float4 u = *reinterpret_cast<const float4*>(&s.U[urow(n, col, vb)]);
+#pragma unroll 4
           for (int t = 1; t <= l; ++t) {
             const float c = s.cA[x + t];
-            const float4 w = *reinterpret_cast<const float4*>(&s.U[s.en[x + t] * vb + col]);
+            const float4 w = *reinterpret_cast<const float4*>(&s.U[urow(s.en[x + t], col, vb)]);
             u.x = fmaf(-c, w.x, u.x);
             u.y = fmaf(-c, w.y, u.y);
             u.z = fmaf(-c, w.z, u.z);
             u.w = fmaf(-c, w.w, u.w);
           }
-          *reinterpret_cast<float4*>(&s.U[n * vb + col]) = u;
+          *reinterpret_cast<float4*>(&s.U[urow(n, col, vb)]) = u;
         }
         __syncthreads();
       }
     }
 
-    // outputs of the chunk's nodes; U rows stored over the parked gamma QS
+    // outputs of the chunk's nodes
     for (int it = tid; it < (p1 - p0) * ncg; it += kBT) {
       const int p = p0 + it / ncg;
       const int col = 4 * (it % ncg);
       const int n = s.ord[p];
       const int x = s.off[p] - e0;
       const int L = s.len[n];
-      float* ug = U + ((size_t)bh * N + n) * dv + c0 + col;
-      float4 acc = *reinterpret_cast<const float4*>(ug);
+      float4 acc = *reinterpret_cast<const float4*>(&s.QS[urow(n, col, vb)]);
+#pragma unroll 4
       for (int t = 0; t < L; ++t) {
         const float c = s.cP[x + t];
-        const float4 w = *reinterpret_cast<const float4*>(&s.U[s.en[x + t] * vb + col]);
+        const float4 w = *reinterpret_cast<const float4*>(&s.U[urow(s.en[x + t], col, vb)]);
         acc = fma4(c, w, acc);
       }
       Elem<TIn>::store4(o, (((size_t)b * N + n) * H + h) * dv + c0 + col, acc);
-      *reinterpret_cast<float4*>(ug) = *reinterpret_cast<const float4*>(&s.U[n * vb + col]);
+      *reinterpret_cast<float4*>(U + ((size_t)bh * N + n) * dv + c0 + col) =
+          *reinterpret_cast<const float4*>(&s.U[urow(n, col, vb)]);
     }
     __syncthreads();
     p0 = p1;
