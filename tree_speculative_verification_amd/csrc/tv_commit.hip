@@ -90,8 +90,8 @@ __global__ __launch_bounds__(kMaxTree) void index_wide_kernel(int N,
 // while they are in flight, then the path's U rows and k entries are staged
 // in LDS (one dependent round trip), and the rank-len(a) update is applied in
 // registers and stored.
-template <typename TK, int DV, int P>
-__global__ __launch_bounds__(kThreads) void commit_kernel(
+template <typename TK, int DV, int P, int NMAX>
+__global__ __launch_bounds__(kThreads, NMAX > kMaxNodes ? 4 : 1) void commit_kernel(
     int H, int N, int dk, int ntiles, const TK* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ U, const int32_t* __restrict__ parents,
     const int32_t* __restrict__ accepted, const float* S_root, float* S_out,
@@ -102,10 +102,11 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   constexpr int CH = 16;                // path entries staged per round
   constexpr int VE = 16 / sizeof(TK);   // k elements per 16-byte load
   static_assert(RT % VE == 0, "tile rows come in whole 16-byte k chunks");
-  __shared__ int spar[kMaxTree];
-  __shared__ float sal[kMaxTree];
-  __shared__ int pidx[kMaxTree];        // path, accepted node first (distance order)
-  __shared__ float coef[kMaxTree];      // D(pidx[i] -> a): product of alpha over distances < i
+  // NMAX: largest tree of the instance (128, or 512 with a second node per thread)
+  __shared__ int spar[NMAX];
+  __shared__ float sal[NMAX];
+  __shared__ int pidx[NMAX];            // path, accepted node first (distance order)
+  __shared__ float coef[NMAX];          // D(pidx[i] -> a): product of alpha over distances < i
   __shared__ float gam;
   __shared__ int slen;
   __shared__ float4 ush[CH][CG];
@@ -125,15 +126,6 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   const int pn = tid < N ? tid : N - 1;
   const int par_v = parents[(size_t)b * N + pn];
   const float a_all = alpha[(size_t)(b * N + pn) * H + h];
-  // trees above kThreads nodes: a second node per thread
-  const int tid2 = tid + kThreads;
-  int par_v2 = -1;
-  float a_all2 = 1.f;
-  if (N > kThreads) {
-    const int pn2 = tid2 < N ? tid2 : N - 1;
-    par_v2 = parents[(size_t)b * N + pn2];
-    a_all2 = alpha[(size_t)(b * N + pn2) * H + h];
-  }
   const int a_in = accepted[b];
   const float4* Sp = reinterpret_cast<const float4*>(S_root + (size_t)bh * dk * DV);
   float4 acc[P];
@@ -146,12 +138,19 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
     spar[tid] = par_v;
     sal[tid] = a_all;
   }
-  if (tid2 < N) {
-    spar[tid2] = par_v2;
-    sal[tid2] = a_all2;
+  bool bad_par = __syncthreads_or(tid < N && (par_v < -1 || par_v >= tid)) != 0;
+  if (NMAX > kThreads && N > kThreads) {  // uniform: a second node per thread
+    // (after the first barrier, so that the load order above stays as it is)
+    const int tid2 = tid + kThreads;
+    const int pn2 = tid2 < N ? tid2 : N - 1;
+    const int par_v2 = parents[(size_t)b * N + pn2];
+    const float a_all2 = alpha[(size_t)(b * N + pn2) * H + h];
+    if (tid2 < N) {
+      spar[tid2] = par_v2;
+      sal[tid2] = a_all2;
+    }
+    bad_par = (__syncthreads_or(tid2 < N && (par_v2 < -1 || par_v2 >= tid2)) != 0) || bad_par;
   }
-  const bool bad_par = __syncthreads_or((tid < N && (par_v < -1 || par_v >= tid)) ||
-                                        (tid2 < N && (par_v2 < -1 || par_v2 >= tid2))) != 0;
   const bool bad_acc = a_in < 0 || a_in >= N;
   if (tid == 0) {
     // walk up from the accepted node; parents[i] < i makes it end within N steps
@@ -173,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
   if (h == 0 && tile == 0) {
     if (tid == 0 && status) status[b] = bad_par ? 1 : (bad_acc ? 2 : 0);
     if (path_out)
-      for (int i = tid; i < N; i += kThreads)
+      for (int i = tid; i < (NMAX > kThreads ? N : min(N, kThreads)); i += kThreads)
         path_out[(size_t)b * N + i] = (!bad_par && !bad_acc && i < L) ? pidx[L - 1 - i] : -1;
   }
   const float g = gam;
@@ -256,9 +255,14 @@ static int commit_launch(int B, int H, int N, int dk, const void* k, const float
   const int ntiles = (dk + RT - 1) / RT;
   const long long nblocks = (long long)B * H * ntiles;
   if (nblocks > 0x7fffffffLL) return static_cast<int>(hipErrorInvalidConfiguration);
-  hipLaunchKernelGGL((commit_kernel<TK, DV, P>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                     H, N, dk, ntiles, static_cast<const TK*>(k), alpha, U, parents, accepted,
-                     S_root, S_out, path_out, status);
+  if (N <= kMaxNodes)
+    hipLaunchKernelGGL((commit_kernel<TK, DV, P, kMaxNodes>), dim3((unsigned)nblocks), dim3(kThreads),
+                       0, stream, H, N, dk, ntiles, static_cast<const TK*>(k), alpha, U, parents,
+                       accepted, S_root, S_out, path_out, status);
+  else
+    hipLaunchKernelGGL((commit_kernel<TK, DV, P, kMaxTree>), dim3((unsigned)nblocks), dim3(kThreads),
+                       0, stream, H, N, dk, ntiles, static_cast<const TK*>(k), alpha, U, parents,
+                       accepted, S_root, S_out, path_out, status);
   return static_cast<int>(hipGetLastError());
 }
 
