@@ -92,6 +92,7 @@ extern "C" {
 #define TV_STATUS_OK 0
 #define TV_STATUS_BAD_PARENTS 1  /* some parents[b][i] outside [-1, i-1] */
 #define TV_STATUS_BAD_ACCEPTED 2 /* accepted[b] outside [0, N) */
+#define TV_STATUS_BAD_PREFIX_LEN 3 /* tree_attention: prefix_len[b] outside [0, P_max] (clamped) */
 
 /*
  * tree_verify -- outputs of all N draft nodes of B sequences x H heads in one
@@ -222,7 +223,43 @@ int tree_commit_verify(int B, int H, int N_prev, int N, int dk, int dv, int dtyp
                        const float* beta, const int32_t* parents, void* o, float* U,
                        int32_t* status, void* stream);
 
-/* Text for a return code (negative) or a status code (0..2). Never NULL. */
+/*
+ * tree_attention -- the full-attention layers of the same hybrid model during
+ * the same tree verification (Twig abstract and Bole abstract: full-attention
+ * layers with a key/value cache of the committed context are interleaved with
+ * the recurrent layers, and verification runs one forward over all draft
+ * nodes).  Draft node n sees the committed prefix and the draft nodes on its
+ * own root path, itself included, as its recurrent state does (Bole
+ * auto-summary worked example); nothing else:
+ *
+ *   o[b, n, hq] = sum_j softmax_j(scale q[b, n, hq] . k_j) v_j
+ *
+ * over j in {cache entries 0 .. prefix_len[b]-1 of key/value head hq / (Hq/Hkv)}
+ * followed by {draft nodes on n's root path}.  Grouped query heads: Hq must be
+ * a multiple of Hkv.  bf16 q/k/v/o, D = 128 only (TV_ERR_HEAD_DIM otherwise,
+ * TV_ERR_MODE for another dtype); softmax in fp32, probabilities rounded to
+ * bf16 for the value product.
+ *
+ *   q         [B, N, Hq, D]       bf16
+ *   k_cache,
+ *   v_cache   [B, Hkv, P_max, D]  bf16, committed context; entries at and past
+ *                                 prefix_len[b] are never read; may be NULL
+ *                                 when P_max == 0
+ *   prefix_len [B] int32          committed length per sequence, 0..P_max
+ *   k_tree,
+ *   v_tree    [B, N, Hkv, D]      bf16, the draft tokens' own keys and values
+ *   parents   [B, N] int32        as tree_verify; N <= TV_MAX_NODES
+ *   scale     softmax scale (e.g. 1/sqrt(D))
+ *   o         [B, N, Hq, D]       OUT, bf16 (round to nearest even)
+ *   status    [B] int32           OUT or NULL: 1 bad parents (treated as -1),
+ *                                 else 3 prefix_len out of range (clamped), else 0
+ */
+int tree_attention(int B, int N, int Hq, int Hkv, int D, int P_max, int dtype, const void* q,
+                   const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+                   const void* k_tree, const void* v_tree, const int32_t* parents, float scale,
+                   void* o, int32_t* status, void* stream);
+
+/* Text for a return code (negative) or a status code (0..3). Never NULL. */
 const char* tv_status_string(int code);
 
 /* ABI version: major * 100 + minor. */

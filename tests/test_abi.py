@@ -29,6 +29,7 @@ def lib():
     L.tree_verify_snapshot.argtypes = [I] * 7 + [P] * 10 + [P]
     L.tree_commit_snapshot.argtypes = [I] * 5 + [P] * 6 + [P]
     L.tree_commit_verify.argtypes = [I] * 8 + [P] * 19
+    L.tree_attention.argtypes = [I] * 7 + [P] * 7 + [ctypes.c_float] + [P] * 3
     L.tv_status_string.restype = ctypes.c_char_p
     return L
 
@@ -43,7 +44,7 @@ def test_header_declares_expected():
     assert declared_functions() == sorted(["tree_verify", "tree_verify_algo", "tree_commit",
                                            "tree_index", "tree_verify_snapshot",
                                            "tree_commit_snapshot", "tree_commit_verify",
-                                           "tv_status_string", "tv_version"])
+                                           "tree_attention", "tv_status_string", "tv_version"])
 
 
 def test_exports_every_declared_symbol(lib):
@@ -56,7 +57,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert lib.tv_version() == 100
-    for code in (0, 1, 2, -1, -2, -3, -4, -5, -6, -107):
+    for code in (0, 1, 2, 3, -1, -2, -3, -4, -5, -6, -107):
         s = lib.tv_status_string(code)
         assert s and s.decode() != "unknown code", code
     assert lib.tv_status_string(12345).decode() == "unknown code"
@@ -185,3 +186,23 @@ def test_product_path_has_no_oracle_import():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "tree_oracle" not in text, f
+
+
+def test_attention_checks(lib):
+    P = FAKE
+    # B N Hq Hkv D P_max dtype | q kc vc plen kt vt parents | scale | o status stream
+    def call(B=1, N=4, Hq=4, Hkv=2, D=128, Pm=8, dtype=1, scale=0.1, **over):
+        p = [P] * 7 + [P, None, None]
+        for i, v in over.items():
+            p[int(i[1:])] = v
+        return lib.tree_attention(B, N, Hq, Hkv, D, Pm, dtype, *p[:7], ctypes.c_float(scale), *p[7:])
+    for i in (0, 3, 4, 5, 6, 7):           # q plen k_tree v_tree parents o
+        assert call(**{f"p{i}": None}) == TV_ERR_NULL, i
+    assert call(p1=None) == TV_ERR_NULL     # caches are required when P_max > 0
+    assert call(p1=None, p2=None, Pm=0, B=0) == TV_ERR_DIMS   # allowed NULL, then the size check
+    assert call(B=0) == TV_ERR_DIMS
+    assert call(N=513) == TV_ERR_DIMS
+    assert call(Hq=6, Hkv=4) == TV_ERR_DIMS  # Hq not a multiple of Hkv
+    assert call(Pm=-1) == TV_ERR_DIMS
+    assert call(D=64) == TV_ERR_HEAD_DIM
+    assert call(dtype=0) == TV_ERR_MODE

@@ -22,7 +22,8 @@ TV_MAX_NODES = 512
 TV_MAX_NODES_SNAPSHOT = 128
 
 SYMBOLS = ["tree_verify", "tree_verify_algo", "tree_commit", "tree_index", "tree_verify_snapshot",
-           "tree_commit_snapshot", "tree_commit_verify", "tv_status_string", "tv_version"]
+           "tree_commit_snapshot", "tree_commit_verify", "tree_attention", "tv_status_string",
+           "tv_version"]
 
 
 class TreeVerifyError(RuntimeError):
@@ -51,6 +52,8 @@ def _load() -> ctypes.CDLL:
     lib.tree_commit_snapshot.restype = I
     lib.tree_commit_verify.argtypes = [I] * 8 + [P] * 9 + [P] * 9 + [P]
     lib.tree_commit_verify.restype = I
+    lib.tree_attention.argtypes = [I] * 7 + [P] * 7 + [ctypes.c_float] + [P] * 3
+    lib.tree_attention.restype = I
     lib.tv_status_string.argtypes = [I]
     lib.tv_status_string.restype = ctypes.c_char_p
     lib.tv_version.argtypes = []
@@ -282,3 +285,32 @@ def commit_verify(k_prev, alpha_prev, U_prev, parents_prev, accepted_prev, S_in,
     if rc != 0:
         raise TreeVerifyError(rc, "tree_commit_verify")
     return S_out, path_out, commit_status, o, U, status
+
+
+def attention(q, k_cache, v_cache, prefix_len, k_tree, v_tree, parents, scale, o=None, status=None,
+              stream=None):
+    """Tree-masked attention: o [B,N,Hq,D] bf16 and status [B] i32 (tree_attention)."""
+    B, N, Hq, D = q.shape
+    Hkv, P_max = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    bf = torch.bfloat16
+    _check(q, "q", (B, N, Hq, D), bf, dev)
+    _check(k_cache, "k_cache", (B, Hkv, P_max, D), bf, dev)
+    _check(v_cache, "v_cache", (B, Hkv, P_max, D), bf, dev)
+    _check(prefix_len, "prefix_len", (B,), torch.int32, dev)
+    _check(k_tree, "k_tree", (B, N, Hkv, D), bf, dev)
+    _check(v_tree, "v_tree", (B, N, Hkv, D), bf, dev)
+    _check(parents, "parents", (B, N), torch.int32, dev)
+    if o is None:
+        o = torch.empty((B, N, Hq, D), dtype=bf, device=dev)
+    if status is None:
+        status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(o, "o", (B, N, Hq, D), bf, dev)
+    _check(status, "status", (B,), torch.int32, dev)
+    rc = LIB.tree_attention(B, N, Hq, Hkv, D, P_max, TV_BF16, _ptr(q), _ptr(k_cache),
+                            _ptr(v_cache), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree),
+                            _ptr(parents), ctypes.c_float(scale), _ptr(o), _ptr(status),
+                            _stream(stream))
+    if rc != 0:
+        raise TreeVerifyError(rc, "tree_attention")
+    return o, status

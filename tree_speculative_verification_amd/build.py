@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 SOURCES = ["tv_api.cpp", "tv_commit.hip", "tv_verify_level.hip", "tv_verify_mfma.hip",
            "tv_snapshot.hip",
-           "tv_verify_blocked.hip"]
+           "tv_verify_blocked.hip", "tv_attention.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -189,11 +189,30 @@ int tree_commit_verify(int B, int H, int N_prev, int N, int dk, int dv, int dtyp
                               mode, q, k, v, alpha, beta, parents, S_out, o, U, status, st));
 }
 
+int tree_attention(int B, int N, int Hq, int Hkv, int D, int P_max, int dtype, const void* q,
+                   const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+                   const void* k_tree, const void* v_tree, const int32_t* parents, float scale,
+                   void* o, int32_t* status, void* stream) {
+  if (!q || !prefix_len || !k_tree || !v_tree || !parents || !o) return TV_ERR_NULL;
+  if (P_max > 0 && (!k_cache || !v_cache)) return TV_ERR_NULL;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv || P_max < 0)
+    return TV_ERR_DIMS;
+  if (D != 128) return TV_ERR_HEAD_DIM;
+  if (dtype != TV_BF16) return TV_ERR_MODE;
+  const long long big = 1LL << 40;
+  if ((long long)B * N > big / ((long long)Hq * D) || (long long)B * Hkv > big / ((long long)(P_max + 1) * D))
+    return TV_ERR_DIMS;
+  return hip_code(tv::launch_tree_attention(B, N, Hq, Hkv, P_max, scale, q, k_cache, v_cache,
+                                            prefix_len, k_tree, v_tree, parents, o, status,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 const char* tv_status_string(int code) {
   switch (code) {
     case TV_OK: return "ok";
     case TV_STATUS_BAD_PARENTS: return "status: a parent index is outside [-1, i-1]";
     case TV_STATUS_BAD_ACCEPTED: return "status: accepted node index is outside [0, N)";
+    case TV_STATUS_BAD_PREFIX_LEN: return "status: prefix_len is outside [0, P_max] (clamped)";
     case TV_ERR_NULL: return "a required pointer is NULL";
     case TV_ERR_DIMS: return "bad sizes: B, H, N must be positive, N <= 512 (128 for the snapshot baseline), sizes must fit";
     case TV_ERR_HEAD_DIM: return "d_k and d_v must be 16, 32, 64 or 128";

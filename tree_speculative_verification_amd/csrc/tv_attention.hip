@@ -1,0 +1,275 @@
+// Tree-masked attention for the full-attention layers of a hybrid model during
+// tree verification: bf16 q/k/v, head dim 128, grouped query heads.
+//
+// Twig abstract and Bole abstract: the model interleaves full-attention layers,
+// which keep a key/value cache of the committed context, with recurrent
+// linear-attention layers, and verification runs one forward over every node
+// of the draft tree.  Draft node n sees what its own root path sees: the
+// committed prefix (the first prefix_len[b] cache entries) and the draft nodes
+// on its root path, itself included (the tree semantics of the Bole
+// auto-summary worked example).  Per query row (node n, query head hq, key/value
+// head hq / G):
+//
+//   o = sum_j softmax_j(scale q.k_j) v_j   over the visible keys j.
+//
+// One workgroup (4 waves) per (sequence b, key/value head, block of 128 query
+// rows); a query row is (node, head in the group), rows in node-major order,
+// and each wave owns 32 of them.  Keys stream through LDS 32 at a time: first
+// the committed prefix, then the draft nodes up to the block's last node.  Per
+// tile, on matrix cores (32x32x16 bf16):
+//   S^T = K Q^T, so a lane owns one query (lane % 32) and 16 of the 32 keys:
+//   the online softmax needs one cross-lane exchange per tile;
+//   O^T += V^T P^T with P rounded to bf16; the key order inside the k-steps is
+//   the accumulator's own row order, read from a transposed V tile in LDS.
+// The next tile's rows are loaded into registers while the current tile is
+// computed, then written to the other of two LDS buffers.
+#include "tv_device.h"
+#include "tv_launch.h"
+
+namespace tv {
+
+namespace {
+
+constexpr int kAT = 256;          // threads per workgroup
+constexpr int kAD = 128;          // head dim
+constexpr int kARows = 128;       // query rows per workgroup
+constexpr int kAKeys = 32;        // keys per tile
+constexpr int kVTS = kAKeys + 4;  // bf16 row stride of the transposed V tile
+constexpr int kAMaskNodes = kARows + 1;        // nodes a row block can touch
+constexpr int kAWords = kMaxTree / 32;         // ancestor words per node
+
+typedef __bf16 abf16x8 __attribute__((ext_vector_type(8)));
+typedef float af32x16 __attribute__((ext_vector_type(16)));
+
+// K tile rows are 256 B (16 chunks of 16 B); chunk c of row r sits at slot
+// c ^ (r & 15), so the lanes of one operand read (32 rows, one chunk) spread
+// over all banks.
+__device__ __forceinline__ int k_slot(int row, int ch) { return ch ^ (row & 15); }
+
+struct AttnLds {
+  uint16_t K[2][kAKeys * kAD];        // key tile, swizzled chunks
+  uint16_t VT[2][kAD * kVTS];         // value tile transposed: [dim][key]
+  uint32_t anc[kAMaskNodes * kAWords];  // inclusive ancestor words of the block's nodes
+  int par[kMaxTree];
+};
+
+__device__ __forceinline__ uint32_t bf16pair(float a, float b) {
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  const v2 x = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  uint32_t r;
+  __builtin_memcpy(&r, &x, 4);
+  return r;
+}
+
+__global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
+    int N, int Hq, int Hkv, int P_max, int nqb, float scale_log2,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ prefix_len,
+    const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
+    const int32_t* __restrict__ parents, uint16_t* __restrict__ o, int32_t* __restrict__ status) {
+  __shared__ __align__(16) AttnLds s;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lm = lane & 31, hi = lane >> 5;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qb = bid % nqb;
+  const int bkv = bid / nqb;
+  const int kvh = bkv % Hkv;
+  const int b = bkv / Hkv;
+  const int G = Hq / Hkv;
+  const int R = N * G;                          // query rows of this (b, kvh)
+  const int r0 = qb * kARows;
+  const int n_lo = r0 / G;
+  const int n_hi = min(N - 1, (min(r0 + kARows, R) - 1) / G);
+  const int W = (N + 31) / 32;
+
+  // this lane's query row and its q operand (d = 16 s + 8 hi + i)
+  const int row = r0 + wave * 32 + lm;
+  const int rc = min(row, R - 1);
+  const int my_n = rc / G;
+  const int hq = kvh * G + rc % G;
+  abf16x8 qop[8];
+  {
+    const uint16_t* qr = q + (((size_t)b * N + my_n) * Hq + hq) * kAD + 8 * hi;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qop[st] = *reinterpret_cast<const abf16x8*>(qr + 16 * st);
+  }
+
+  // ---- tree: parents (validated, bad ones treated as -1), ancestor words ----
+  int P = prefix_len[b];
+  const bool bad_len = P < 0 || P > P_max;
+  P = min(max(P, 0), P_max);
+  bool my_bad = false;
+  for (int i = tid; i < N; i += kAT) {
+    int p = parents[(size_t)b * N + i];
+    if (p < -1 || p >= i) {
+      my_bad = true;
+      p = -1;
+    }
+    s.par[i] = p;
+  }
+  const bool bad = __syncthreads_or(my_bad) != 0;
+  if (qb == 0 && kvh == 0 && tid == 0 && status) status[b] = bad ? 1 : (bad_len ? 3 : 0);
+  for (int i = tid; i <= n_hi - n_lo; i += kAT) {
+    uint32_t* a = s.anc + i * kAWords;
+    for (int w = 0; w < W; ++w) a[w] = 0u;
+    for (int j = n_lo + i; j >= 0; j = s.par[j]) a[j >> 5] |= 1u << (j & 31);
+  }
+
+  // ---- key tiles: prefix tiles [0, TP), then tree tiles up to node n_hi ----
+  const int TP = (P + kAKeys - 1) / kAKeys;
+  const int T = TP + n_hi / kAKeys + 1;
+  const size_t cache_bh = ((size_t)b * Hkv + kvh) * P_max;
+  // thread's two 16-byte chunks of a tile: chunk c = tid + 256 u, key c / 16,
+  // dims 8 (c % 16) .. + 7
+  uint4 kreg[2], vreg[2];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + kAT * u;
+      const int key = c >> 4, ch = c & 15;
+      const uint16_t *kp, *vp;
+      if (t < TP) {
+        const size_t r = cache_bh + min(t * kAKeys + key, P - 1);
+        kp = kc + r * kAD;
+        vp = vc + r * kAD;
+      } else {
+        const int jn = min((t - TP) * kAKeys + key, N - 1);
+        const size_t r = ((size_t)b * N + jn) * Hkv + kvh;
+        kp = kt + r * kAD;
+        vp = vt + r * kAD;
+      }
+      kreg[u] = *reinterpret_cast<const uint4*>(kp + 8 * ch);
+      vreg[u] = *reinterpret_cast<const uint4*>(vp + 8 * ch);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + kAT * u;
+      const int key = c >> 4, ch = c & 15;
+      *reinterpret_cast<uint4*>(&s.K[buf][key * kAD + k_slot(key, ch) * 8]) = kreg[u];
+      const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s.VT[buf][(8 * ch + 2 * e) * kVTS + key] = static_cast<uint16_t>(w[e] & 0xffffu);
+        s.VT[buf][(8 * ch + 2 * e + 1) * kVTS + key] = static_cast<uint16_t>(w[e] >> 16);
+      }
+    }
+  };
+
+  af32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();  // first tile and the ancestor words visible
+  for (int t = 0; t < T; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < T) load_tile(t + 1);
+    // S^T = K Q^T: this lane holds keys 8 (r/4) + 4 hi + r%4 of the tile for query lm
+    af32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    const uint16_t* Kr = s.K[buf] + lm * kAD;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const abf16x8 a = *reinterpret_cast<const abf16x8*>(Kr + k_slot(lm, 2 * st + hi) * 8);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], sacc, 0, 0, 0);
+    }
+    // visibility: prefix keys below P; tree keys on the query node's root path
+    uint32_t vis;
+    if (t < TP) {
+      const int left = P - t * kAKeys;
+      vis = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
+    } else {
+      vis = s.anc[(my_n - n_lo) * kAWords + (t - TP)];
+    }
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
+      sacc[r] = ((vis >> key) & 1u) ? sacc[r] * scale_log2 : -__builtin_inff();
+      mt = fmaxf(mt, sacc[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    uint32_t pw[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = exp2f(sacc[r] - m_new), p1 = exp2f(sacc[r + 1] - m_new);
+      psum += p0 + p1;
+      pw[r >> 1] = bf16pair(p0, p1);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    // O^T += V^T P^T; k-step h2 covers accumulator rows 8 h2 .. 8 h2 + 7, i.e.
+    // keys 16 h2 + 4 hi + (0..3) and 16 h2 + 8 + 4 hi + (0..3)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      abf16x8 pb;
+      __builtin_memcpy(&pb, &pw[4 * h2], 16);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint16_t* vr = s.VT[buf] + (32 * dt + lm) * kVTS + 16 * h2 + 4 * hi;
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 8);
+        const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        abf16x8 va;
+        __builtin_memcpy(&va, &vv, 16);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
+      }
+    }
+    if (t + 1 < T) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: this lane holds dims 32 dt + 8 j + 4 hi + (0..3) ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.f / l_tot;
+  if (row < R) {
+    uint16_t* orow = o + (((size_t)b * N + my_n) * Hq + hq) * kAD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint2 w;
+        w.x = bf16pair(oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv);
+        w.y = bf16pair(oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * j + 4 * hi) = w;
+      }
+  }
+}
+
+}  // namespace
+
+int launch_tree_attention(int B, int N, int Hq, int Hkv, int P_max, float scale, const void* q,
+                          const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+                          const void* k_tree, const void* v_tree, const int32_t* parents, void* o,
+                          int32_t* status, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  const long long rows = (long long)N * G;
+  const int nqb = (int)((rows + kARows - 1) / kARows);
+  const long long nblocks = (long long)B * Hkv * nqb;
+  if (nblocks > 0x7fffffffLL) return static_cast<int>(hipErrorInvalidConfiguration);
+  const float scale_log2 = scale * 1.4426950408889634f;  // log2(e): softmax in base 2
+  hipLaunchKernelGGL(tree_attention_kernel, dim3((unsigned)nblocks), dim3(kAT), 0, stream, N, Hq,
+                     Hkv, P_max, nqb, scale_log2, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                     prefix_len, static_cast<const uint16_t*>(k_tree),
+                     static_cast<const uint16_t*>(v_tree), parents, static_cast<uint16_t*>(o),
+                     status);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace tv

@@ -26,6 +26,12 @@ int launch_verify_blocked(int B, int H, int N, int dk, int dv, int dtype, int mo
                           const int32_t* parents, const float* S_root, void* o, float* U,
                           int32_t* status, hipStream_t stream);
 
+// Tree-masked attention (tv_attention.hip): bf16, head dim 128.
+int launch_tree_attention(int B, int N, int Hq, int Hkv, int P_max, float scale, const void* q,
+                          const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+                          const void* k_tree, const void* v_tree, const int32_t* parents, void* o,
+                          int32_t* status, hipStream_t stream);
+
 // The previous step's commit, applied to the state on the fly by the fused
 // verification (arrays as tree_commit takes them, N = the previous tree's size).
 struct PrevCommit {

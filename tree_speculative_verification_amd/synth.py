@@ -281,6 +281,86 @@ def make_custom(parents, accepted, H, dk, dv, mode=GDN, dtype=F32, seed=0,
                      q=q, k=k, v=v, alpha=alpha, beta=beta, S_root=S_root)
 
 
+@dataclasses.dataclass
+class AttnBatch:
+    """Host arrays for one tree_attention call (bf16-representable float32).
+
+    parents [B, N]; q [B, N, Hq, D]; k_cache, v_cache [B, Hkv, P_max, D];
+    prefix_len [B] int32; k_tree, v_tree [B, N, Hkv, D]; scale.
+    """
+
+    parents: np.ndarray
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    prefix_len: np.ndarray
+    k_tree: np.ndarray
+    v_tree: np.ndarray
+    scale: float
+
+
+# The attention workload: the 64-node trees of workload 4 through a
+# full-attention layer with grouped query heads and a ragged committed context.
+ATTN_CONFIG = dict(B=32, N=64, Hq=32, Hkv=8, D=128, P_max=4096)
+ATTN_NAME = ("tree-attention-bf16 B32 N64 Hq32 Hkv8 D128 prefix U[2048,4096] "
+             "random tree depth<=8 fanout<=4")
+
+
+def make_attention_inputs(seed: int = 7, B: Optional[int] = None, N: Optional[int] = None,
+                          Hq: Optional[int] = None, Hkv: Optional[int] = None,
+                          D: Optional[int] = None, P_max: Optional[int] = None,
+                          parents: Optional[np.ndarray] = None,
+                          prefix_len: Optional[np.ndarray] = None) -> AttnBatch:
+    """Seeded inputs for tree_attention (defaults: the attention workload).
+
+    Draw order: trees (depth <= 8, <= 4 children, as workload 4), prefix
+    lengths (uniform in [P_max/2, P_max]), q, k_cache, v_cache, k_tree, v_tree,
+    all N(0, 1) rounded to bf16; scale = 1/sqrt(D).
+    """
+    c = ATTN_CONFIG
+    B = c["B"] if B is None else B
+    N = c["N"] if N is None else N
+    Hq = c["Hq"] if Hq is None else Hq
+    Hkv = c["Hkv"] if Hkv is None else Hkv
+    D = c["D"] if D is None else D
+    P_max = c["P_max"] if P_max is None else P_max
+    rng = np.random.default_rng(seed)
+    if parents is None:
+        parents = np.stack([random_tree(rng, N, max_depth=8, max_children=4) for _ in range(B)])
+    parents = np.asarray(parents, dtype=np.int32)
+    if prefix_len is None:
+        prefix_len = rng.integers(P_max // 2, P_max + 1, size=B)
+    prefix_len = np.asarray(prefix_len, dtype=np.int32)
+
+    def g(shape):
+        return round_bf16(rng.standard_normal(size=shape, dtype=np.float32))
+
+    q = g((B, N, Hq, D))
+    k_cache = g((B, Hkv, P_max, D))
+    v_cache = g((B, Hkv, P_max, D))
+    k_tree = g((B, N, Hkv, D))
+    v_tree = g((B, N, Hkv, D))
+    return AttnBatch(parents=parents, q=q, k_cache=k_cache, v_cache=v_cache,
+                     prefix_len=prefix_len, k_tree=k_tree, v_tree=v_tree,
+                     scale=float(1.0 / np.sqrt(D)))
+
+
+def attention_to_torch(batch: AttnBatch, device="cuda"):
+    """Device tensors of an AttnBatch (bf16 bit-exact copies, int32 indices)."""
+    import torch
+
+    def vals(x):
+        bits = bf16_bits(x).view(np.int16)
+        return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(device)
+
+    return dict(q=vals(batch.q), k_cache=vals(batch.k_cache), v_cache=vals(batch.v_cache),
+                prefix_len=i32(batch.prefix_len), k_tree=vals(batch.k_tree),
+                v_tree=vals(batch.v_tree), parents=i32(batch.parents), scale=batch.scale)
+
+
 def to_torch(batch: TreeBatch, device="cuda"):
     """Copies a batch to `device` as the tensors the library takes.
 
