@@ -157,6 +157,129 @@ def cpu_baseline(bt, max_seqs, reps):
                       f"{cpu_model}"}
 
 
+# ------------------------------------------------------ tree attention leg
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ATTN_METRIC = "verified tree nodes/s per full-attention layer (1 GPU) + % of HBM roofline"
+
+
+def attention_work(bt):
+    """Algorithmic bytes and flops of one tree_attention launch.
+
+    Bytes: q and o, the prefix rows of both caches that are visible (each
+    read once per key/value head), the tree's k and v rows, prefix_len and
+    parents.  Flops: 4 D per (query row, visible key) (q.k and p v)."""
+    B, N, Hq, D = bt.q.shape
+    Hkv = bt.k_cache.shape[1]
+    depth = np.stack([synth.depths_of(p) for p in bt.parents])          # [B, N]
+    nbytes = (2 * B * N * Hq * D * 2 + int(bt.prefix_len.sum()) * Hkv * D * 2 * 2
+              + B * N * Hkv * D * 2 * 2 + B * 4 + B * N * 4)
+    keys = bt.prefix_len[:, None] + depth + 1                           # visible keys per node
+    flops = 4 * D * Hq * int(keys.sum())
+    return int(nbytes), int(flops)
+
+
+_ATTN_BATCH = None
+
+
+def _oracle_attn_seq(bh):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import tree_attention as A
+    threadpool_limits(1)  # one BLAS thread per worker process
+    b, h = bh
+    bt = _ATTN_BATCH
+    A.tree_attention(bt.parents, bt.q, bt.k_cache, bt.v_cache, bt.prefix_len, bt.k_tree,
+                     bt.v_tree, bt.scale, seqs=[b], heads=[h])
+
+
+def attention_cpu_baseline(bt, pairs):
+    """The fp64 oracle over `pairs` (sequence, query head) of the workload, one
+    process per core; scaled to nodes/s of the whole layer (every head)."""
+    global _ATTN_BATCH
+    import multiprocessing as mp
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    _ATTN_BATCH = bt
+    B, N, Hq, _ = bt.q.shape
+    work = [(b, h) for b in range(B) for h in range(Hq)][:pairs]
+    cores = min(len(os.sched_getaffinity(0)), 16, len(work))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        list(pool.imap_unordered(_oracle_attn_seq, work))
+    wall = time.perf_counter() - t0
+    # one sequence's N nodes need all Hq heads: nodes/s = pairs * N / Hq / wall
+    return {"value": len(work) * N / Hq / wall, "unit": "nodes/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(work)} (sequence, query head) pairs of the workload, all {N} nodes "
+                      f"each (fp64 masked softmax per node), scaled to whole nodes (all {Hq} "
+                      f"heads); wall {wall:.2f} s on {cores} worker processes"}
+
+
+def attention_main(a):
+    bt = synth.make_attention_inputs()
+    cpu = None if a.no_cpu_baseline else attention_cpu_baseline(bt, a.cpu_attn_pairs)
+
+    import torch
+    from tree_speculative_verification_amd import binding as tvb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = synth.attention_to_torch(bt, dev)
+    B, N, Hq, D = bt.q.shape
+    set_bytes = sum(x.numel() * x.element_size() for x in base.values() if torch.is_tensor(x))
+    R = max(2, -(-(1 << 30) // set_bytes))
+    sets = [base] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in base.items()}
+                     for _ in range(R - 1)]
+    for t in sets:
+        t["o"] = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=dev)
+        t["st"] = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        t = sets[i % R]
+        tvb.attention(t["q"], t["k_cache"], t["v_cache"], t["prefix_len"], t["k_tree"],
+                      t["v_tree"], t["parents"], t["scale"], o=t["o"], status=t["st"],
+                      stream=stream)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if any(t["st"].any().item() for t in sets):
+        raise RuntimeError("device status reported bad input rows")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    nbytes, flops = attention_work(bt)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": ATTN_METRIC, "value": round(B * N / (ms * 1e-3), 1), "unit": "nodes/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": synth.ATTN_NAME, "B": B, "N": N, "Hq": Hq,
+                   "Hkv": bt.k_cache.shape[1], "D": D, "P_max": bt.k_cache.shape[2],
+                   "mean_prefix": round(float(bt.prefix_len.mean()), 1),
+                   "timing": f"HIP events around K launches on the launch stream; ring of {R} "
+                             "input copies (>= 1 GB) so every launch reads cold caches"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "tree_attention_kernel", "algorithmic_bytes": nbytes},
+        "mfma": {"achieved_TFLOPs": round(tfs, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops,
+                 "arithmetic_intensity_flop_per_byte": round(flops / nbytes, 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------- GPU timing
 
 def copy_calibration():
@@ -227,6 +350,11 @@ def main(argv=None):
                     help="passes of the CPU oracle over the sampled sequences")
     ap.add_argument("--no-snapshot-baseline", action="store_true",
                     help="skip timing the per-node-snapshot baseline kernels")
+    ap.add_argument("--attention", action="store_true",
+                    help="time tree_attention (the hybrid's full-attention layers) on its "
+                         "workload instead of the verification pipeline")
+    ap.add_argument("--cpu-attn-pairs", type=int, default=256,
+                    help="(sequence, head) pairs of the attention oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (three times, caches "
                          "evicted by a read-only pass before each), to scale rocprofv3's "
@@ -241,6 +369,8 @@ def main(argv=None):
         return 2
     if int(os.environ.get("RANK", "0")) != 0:
         return 0
+    if a.attention:
+        return attention_main(a)
 
     bt = synth.make_inputs(a.workload)
     cpu = None if a.no_cpu_baseline else cpu_baseline(bt, a.cpu_seqs, a.cpu_reps)

@@ -19,10 +19,11 @@
 // tile, on matrix cores (32x32x16 bf16):
 //   S^T = K Q^T, so a lane owns one query (lane % 32) and 16 of the 32 keys:
 //   the online softmax needs one cross-lane exchange per tile;
-//   O^T += V^T P^T with P rounded to bf16; the key order inside the k-steps is
-//   the accumulator's own row order, read from a transposed V tile in LDS.
-// The next tile's rows are loaded into registers while the current tile is
-// computed, then written to the other of two LDS buffers.
+//   O += P V with P rounded to bf16: the score accumulator is already P's
+//   operand layout when the k-steps take keys in the accumulator's row order,
+//   and V is read in that order from a row-major tile in LDS.
+// A tile's rows are loaded into registers three tiles ahead and written to the
+// other of two LDS buffers while the tile before it is computed.
 #include "tv_device.h"
 #include "tv_launch.h"
 
@@ -34,7 +35,7 @@ constexpr int kAT = 256;          // threads per workgroup
 constexpr int kAD = 128;          // head dim
 constexpr int kARows = 128;       // query rows per workgroup
 constexpr int kAKeys = 32;        // keys per tile
-constexpr int kVTS = kAKeys + 4;  // bf16 row stride of the transposed V tile
+constexpr int kVS = kAD + 8;       // bf16 row stride of the V tile (rows 4 apart on other banks)
 constexpr int kAMaskNodes = kARows + 1;        // nodes a row block can touch
 constexpr int kAWords = kMaxTree / 32;         // ancestor words per node
 
@@ -48,7 +49,7 @@ __device__ __forceinline__ int k_slot(int row, int ch) { return ch ^ (row & 15);
 
 struct AttnLds {
   uint16_t K[2][kAKeys * kAD];        // key tile, swizzled chunks
-  uint16_t VT[2][kAD * kVTS];         // value tile transposed: [dim][key]
+  uint16_t V[2][kAKeys * kVS];        // value tile, row-major, padded rows
   uint32_t anc[kAMaskNodes * kAWords];  // inclusive ancestor words of the block's nodes
   int par[kMaxTree];
 };
@@ -119,44 +120,54 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   // ---- key tiles: prefix tiles [0, TP), then tree tiles up to node n_hi ----
   const int TP = (P + kAKeys - 1) / kAKeys;
   const int T = TP + n_hi / kAKeys + 1;
+  // the loop runs in steps of three tiles; tiles past T are fully masked
+  // (their loads repeat tile T - 1), so the loop body has no branches and the
+  // wait counts before each LDS store stay exact
+  const int T3 = (T + 2) / 3 * 3;
   const size_t cache_bh = ((size_t)b * Hkv + kvh) * P_max;
-  // thread's two 16-byte chunks of a tile: chunk c = tid + 256 u, key c / 16,
-  // dims 8 (c % 16) .. + 7
-  uint4 kreg[2], vreg[2];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + kAT * u;
-      const int key = c >> 4, ch = c & 15;
-      const uint16_t *kp, *vp;
-      if (t < TP) {
-        const size_t r = cache_bh + min(t * kAKeys + key, P - 1);
-        kp = kc + r * kAD;
-        vp = vc + r * kAD;
-      } else {
-        const int jn = min((t - TP) * kAKeys + key, N - 1);
-        const size_t r = ((size_t)b * N + jn) * Hkv + kvh;
-        kp = kt + r * kAD;
-        vp = vt + r * kAD;
-      }
-      kreg[u] = *reinterpret_cast<const uint4*>(kp + 8 * ch);
-      vreg[u] = *reinterpret_cast<const uint4*>(vp + 8 * ch);
+  // Thread's two 16-byte chunks of a tile: chunk c = tid + 256 u, key c / 16,
+  // dims 8 (c % 16) .. + 7.  Three register sets: a tile's rows are loaded
+  // three iterations before the iteration that computes it, and written to
+  // LDS one iteration before.
+  // source rows of this thread's chunk u (0, 1) of tile t
+  auto src_rows = [&](int t, int u, const uint16_t*& kp, const uint16_t*& vp) {
+    t = min(t, T - 1);
+    const int c = tid + kAT * u;
+    const int key = c >> 4, ch = c & 15;
+    if (t < TP) {
+      const size_t r = cache_bh + min(t * kAKeys + key, P - 1);
+      kp = kc + r * kAD + 8 * ch;
+      vp = vc + r * kAD + 8 * ch;
+    } else {
+      const int jn = min((t - TP) * kAKeys + key, N - 1);
+      const size_t r = ((size_t)b * N + jn) * Hkv + kvh;
+      kp = kt + r * kAD + 8 * ch;
+      vp = vt + r * kAD + 8 * ch;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + kAT * u;
-      const int key = c >> 4, ch = c & 15;
-      *reinterpret_cast<uint4*>(&s.K[buf][key * kAD + k_slot(key, ch) * 8]) = kreg[u];
-      const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s.VT[buf][(8 * ch + 2 * e) * kVTS + key] = static_cast<uint16_t>(w[e] & 0xffffu);
-        s.VT[buf][(8 * ch + 2 * e + 1) * kVTS + key] = static_cast<uint16_t>(w[e] >> 16);
-      }
-    }
+  auto store_chunk = [&](int buf, int u, uint4 kv, uint4 vv) {
+    const int c = tid + kAT * u;
+    const int key = c >> 4, ch = c & 15;
+    *reinterpret_cast<uint4*>(&s.K[buf][key * kAD + k_slot(key, ch) * 8]) = kv;
+    *reinterpret_cast<uint4*>(&s.V[buf][key * kVS + 8 * ch]) = vv;
   };
+  // three register sets (X = A, B, C) of two chunks of K and V each
+  uint4 kA0, kA1, vA0, vA1, kB0, kB1, vB0, vB1, kC0, kC1, vC0, vC1;
+#define TV_LOAD(X, t)                                              \
+  {                                                                \
+    const uint16_t *kp_, *vp_;                                     \
+    src_rows((t), 0, kp_, vp_);                                    \
+    k##X##0 = *reinterpret_cast<const uint4*>(kp_);                \
+    v##X##0 = *reinterpret_cast<const uint4*>(vp_);                \
+    src_rows((t), 1, kp_, vp_);                                    \
+    k##X##1 = *reinterpret_cast<const uint4*>(kp_);                \
+    v##X##1 = *reinterpret_cast<const uint4*>(vp_);                \
+  }
+#define TV_STORE(X, t)                                             \
+  {                                                                \
+    store_chunk((t) & 1, 0, k##X##0, v##X##0);                     \
+    store_chunk((t) & 1, 1, k##X##1, v##X##1);                     \
+  }
 
   af32x16 oacc[4];
 #pragma unroll
@@ -165,12 +176,9 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();  // first tile and the ancestor words visible
-  for (int t = 0; t < T; ++t) {
+  // one key tile from LDS buffer t & 1 into the running softmax and O^T
+  auto compute_tile = [&](int t) {
     const int buf = t & 1;
-    if (t + 1 < T) load_tile(t + 1);
     // S^T = K Q^T: this lane holds keys 8 (r/4) + 4 hi + r%4 of the tile for query lm
     af32x16 sacc;
 #pragma unroll
@@ -182,11 +190,11 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], sacc, 0, 0, 0);
     }
     // visibility: prefix keys below P; tree keys on the query node's root path
-    uint32_t vis;
+    uint32_t vis = 0u;
     if (t < TP) {
       const int left = P - t * kAKeys;
       vis = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
-    } else {
+    } else if (t < T) {
       vis = s.anc[(my_n - n_lo) * kAWords + (t - TP)];
     }
     float mt = -__builtin_inff();
@@ -197,57 +205,102 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
       mt = fmaxf(mt, sacc[r]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+    // The reference maximum moves only when some query of the wave gains more
+    // than 2^8 on it (one uniform branch): until then the probabilities stay
+    // below 256, exact to fp32 rounding, and O^T and l need no rescaling.
+    if (__any(mt > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      // O's lane holds queries 8 (r/4) + 4 hi + r%4; their factors sit in
+      // lanes of those queries
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ar = __shfl(alpha, 8 * (r >> 2) + 4 * hi + (r & 3));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[dt][r] *= ar;
+      }
+    }
     float psum = 0.f;
     uint32_t pw[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2f(sacc[r] - m_new), p1 = exp2f(sacc[r + 1] - m_new);
+      const float p0 = exp2f(sacc[r] - m_run), p1 = exp2f(sacc[r + 1] - m_run);
       psum += p0 + p1;
       pw[r >> 1] = bf16pair(p0, p1);
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    // O^T += V^T P^T; k-step h2 covers accumulator rows 8 h2 .. 8 h2 + 7, i.e.
-    // keys 16 h2 + 4 hi + (0..3) and 16 h2 + 8 + 4 hi + (0..3)
+    l_run += psum;
+    // O += P V on matrix cores.  P is already the A operand: k-step h2 of lane
+    // (query lm, hi) holds keys 16 h2 + 4 hi + (0..3) and 16 h2 + 8 + 4 hi +
+    // (0..3) (its accumulator rows 8 h2 .. 8 h2 + 7); the B operand takes the
+    // same keys of value column 32 dt + lm from the row-major V tile.
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      abf16x8 pb;
-      __builtin_memcpy(&pb, &pw[4 * h2], 16);
+      abf16x8 pa;
+      __builtin_memcpy(&pa, &pw[4 * h2], 16);
+      const uint16_t* vr = s.V[buf] + (16 * h2 + 4 * hi) * kVS + lm;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* vr = s.VT[buf] + (32 * dt + lm) * kVTS + 16 * h2 + 4 * hi;
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 8);
-        const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
-        abf16x8 va;
-        __builtin_memcpy(&va, &vv, 16);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
+        const uint16_t* vc0 = vr + 32 * dt;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          w[i] = static_cast<uint32_t>(vc0[(2 * i) * kVS]) |
+                 (static_cast<uint32_t>(vc0[(2 * i + 1) * kVS]) << 16);
+          w[2 + i] = static_cast<uint32_t>(vc0[(8 + 2 * i) * kVS]) |
+                     (static_cast<uint32_t>(vc0[(8 + 2 * i + 1) * kVS]) << 16);
+        }
+        abf16x8 vb;
+        __builtin_memcpy(&vb, w, 16);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, oacc[dt], 0, 0, 0);
       }
     }
-    if (t + 1 < T) store_tile(buf ^ 1);
-    __syncthreads();
-  }
+  };
 
-  // ---- normalise and store: this lane holds dims 32 dt + 8 j + 4 hi + (0..3) ----
+  // q (and the tree's loads) have landed before the pipeline starts, so no
+  // wait inside the loop is held up by them
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  // pipeline: tile t + 3 loaded, tile t computed, tile t + 1 stored, barrier;
+  // set X holds tile t + 1 (to store) and set Y receives tile t + 3 (its
+  // previous tile t is in LDS already)
+  TV_LOAD(A, 0)
+  TV_LOAD(B, 1)
+  TV_LOAD(C, 2)
+  TV_STORE(A, 0)
+  __syncthreads();  // first tile and the ancestor words visible
+#define TV_ATTN_STEP(t, X, Y) \
+  do {                        \
+    TV_LOAD(Y, (t) + 3)       \
+    compute_tile(t);          \
+    TV_STORE(X, (t) + 1)      \
+    __syncthreads();          \
+  } while (0)
+  for (int t = 0; t < T3; t += 3) {
+    TV_ATTN_STEP(t, B, A);
+    TV_ATTN_STEP(t + 1, C, B);
+    TV_ATTN_STEP(t + 2, A, C);
+  }
+#undef TV_ATTN_STEP
+#undef TV_LOAD
+#undef TV_STORE
+
+  // ---- normalise and store: this lane holds value column 32 dt + lm of the
+  // wave's queries 8 (r/4) + 4 hi + r%4 ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
-  if (row < R) {
-    uint16_t* orow = o + (((size_t)b * N + my_n) * Hq + hq) * kAD;
+  const float inv = 1.f / l_tot;  // for query lm
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int r = 0; r < 16; ++r) {
+    const int qi = 8 * (r >> 2) + 4 * hi + (r & 3);
+    const float iq = __shfl(inv, qi);
+    const int rq = r0 + wave * 32 + qi;
+    if (rq < R) {
+      const int nq = rq / G;
+      const int hqq = kvh * G + rq % G;
+      uint16_t* orow = o + (((size_t)b * N + nq) * Hq + hqq) * kAD + lm;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint2 w;
-        w.x = bf16pair(oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv);
-        w.y = bf16pair(oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * j + 4 * hi) = w;
-      }
+      for (int dt = 0; dt < 4; ++dt) orow[32 * dt] = f32_to_bf16(oacc[dt][r] * iq);
+    }
   }
 }
 
