@@ -51,6 +51,7 @@ KERNEL_SOURCES = {
     "fused": [_CSRC + "tv_verify_mfma.hip", _CSRC + "tv_device.h"],
     "commit": [_CSRC + "tv_commit.hip", _CSRC + "tv_device.h"],
 }
+KERNEL_SOURCES["attention"] = [_CSRC + "tv_attention.hip", _CSRC + "tv_device.h"]
 # trees above 128 nodes: blocked verification, and commit + blocked verify as the step
 KERNEL_SOURCES_LARGE = {
     "verify": [_CSRC + "tv_verify_blocked.hip", _CSRC + "tv_device.h"],
@@ -102,7 +103,7 @@ def measured_traffic(kind, workload):
     except (OSError, ValueError):
         return None
     r = rec.get(f"{kind}_w{workload}")
-    large = synth.CONFIGS[workload]["N"] > SMALL_TREE
+    large = workload in synth.CONFIGS and synth.CONFIGS[workload]["N"] > SMALL_TREE
     if not r or r.get("source_sha") != sources_sha(kind, large):
         return None
     return r.get("bytes_per_launch")
@@ -269,7 +270,8 @@ def attention_main(a):
                    "timing": f"HIP events around K launches on the launch stream; ring of {R} "
                              "input copies (>= 1 GB) so every launch reads cold caches"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("attention", "attn"),
                      "kernel": "tree_attention_kernel", "algorithmic_bytes": nbytes},
         "mfma": {"achieved_TFLOPs": round(tfs, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
                  "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops,
