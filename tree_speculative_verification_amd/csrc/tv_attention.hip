@@ -40,6 +40,9 @@ constexpr int kAMaskNodes = kARows + 1;        // nodes a row block can touch
 constexpr int kAWords = kMaxTree / 32;         // ancestor words per node
 
 typedef __bf16 abf16x8 __attribute__((ext_vector_type(8)));
+typedef short atr4 __attribute__((ext_vector_type(4)));
+typedef short atr8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) atr4 lds_tr4;
 typedef float af32x16 __attribute__((ext_vector_type(16)));
 
 // K tile rows are 256 B (16 chunks of 16 B); chunk c of row r sits at slot
@@ -198,10 +201,10 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
       vis = s.anc[(my_n - n_lo) * kAWords + (t - TP)];
     }
     float mt = -__builtin_inff();
+    const uint32_t vh = vis >> (4 * hi);  // bit 8 (r/4) + r%4: key 8 (r/4) + 4 hi + r%4
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
-      sacc[r] = ((vis >> key) & 1u) ? sacc[r] * scale_log2 : -__builtin_inff();
+      sacc[r] = ((vh >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] * scale_log2 : -__builtin_inff();
       mt = fmaxf(mt, sacc[r]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -235,24 +238,26 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
     // (query lm, hi) holds keys 16 h2 + 4 hi + (0..3) and 16 h2 + 8 + 4 hi +
     // (0..3) (its accumulator rows 8 h2 .. 8 h2 + 7); the B operand takes the
     // same keys of value column 32 dt + lm from the row-major V tile.
+    // The B operand comes from LDS transpose reads: within each 16-lane group
+    // g, lane i receives element i % 4 of the 8-byte chunks addressed by lanes
+    // i/4, i/4 + 4, i/4 + 8, i/4 + 12.  So lane (q = lane % 4, j = lane/4 % 4)
+    // of group g addresses columns 16 (g % 2) + 4 q .. + 3 of key row
+    // 4 (g / 2) + j (+ 16 h2, + 8 for the second half of the k-step), and lane
+    // (column n, hi) gets keys 4 hi + (0..3) of its column.
+    const uint16_t* vtr = s.V[buf] + (4 * (lane >> 5) + ((lane >> 2) & 3)) * kVS +
+                          16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       abf16x8 pa;
       __builtin_memcpy(&pa, &pw[4 * h2], 16);
-      const uint16_t* vr = s.V[buf] + (16 * h2 + 4 * hi) * kVS + lm;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* vc0 = vr + 32 * dt;
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          w[i] = static_cast<uint32_t>(vc0[(2 * i) * kVS]) |
-                 (static_cast<uint32_t>(vc0[(2 * i + 1) * kVS]) << 16);
-          w[2 + i] = static_cast<uint32_t>(vc0[(8 + 2 * i) * kVS]) |
-                     (static_cast<uint32_t>(vc0[(8 + 2 * i + 1) * kVS]) << 16);
-        }
-        abf16x8 vb;
-        __builtin_memcpy(&vb, w, 16);
+        const uint16_t* v0 = vtr + 16 * h2 * kVS + 32 * dt;
+        // (C casts: the generic pointer into the LDS tile to an LDS pointer)
+        const atr4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4*)(v0));
+        const atr4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4*)(v0 + 8 * kVS));
+        const atr8 w = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        const abf16x8 vb = __builtin_bit_cast(abf16x8, w);
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, oacc[dt], 0, 0, 0);
       }
     }
