@@ -87,6 +87,17 @@ def test_deep_chain(N):
     _check(_batch(np.stack([_chain(N)] * 2), H=1, seed=N))
 
 
+@pytest.mark.parametrize("N,dtype,d", [(77, synth.BF16, 128), (78, synth.BF16, 128),
+                                       (52, synth.F32, 64), (53, synth.F32, 64)])
+def test_resident_limit(N, dtype, d):
+    """Chains whose N(N+1)/2 path entries sit just inside and just outside what
+    LDS holds (3040 entries with bf16 inputs, 1400 with fp32): inside, the
+    inverse of I + A is built level by level over the whole chain and each
+    column block is one gather; outside, the chunked level solve."""
+    par = np.stack([_chain(N), np.full(N, -1, np.int32)])  # a chain, and N lone roots
+    _check(_batch(par, H=2, d=d, dtype=dtype, seed=N), algo=BLOCKED)
+
+
 @pytest.mark.parametrize("N,depth", [(400, 120), (256, 40)])
 def test_deep_random(N, depth):
     rng = np.random.default_rng(N + depth)

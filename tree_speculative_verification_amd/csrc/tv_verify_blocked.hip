@@ -15,7 +15,7 @@
 //
 // The solve is blocked so that any tree fits on chip.  The tree's path
 // entries (node n, ancestor j) are laid out node after node with nodes sorted
-// by depth, and processed in chunks of at most kBEnt entries: a chunk's
+// by depth, and processed in chunks of as many entries as LDS holds: a chunk's
 // entries get their Gram values and decays, then the chunk's nodes are solved
 // one depth level at a time (a node's ancestors all sit in earlier levels, so
 // they are final by then), then their outputs are gathered.  Only the chunk's
@@ -23,10 +23,10 @@
 // go through the same code; a wide tree is a few chunks and one level step
 // per depth.
 //
-// One workgroup of 512 threads per (sequence b, head h, block of up to 32
-// value columns):
+// One workgroup of 1024 threads per (sequence b, head h):
 //   1. tree index: pointer jumping gives each node's path length and gamma;
 //      nodes are then sorted by depth (counting sort) and given entry offsets;
+// then, for each block of up to 32 value columns:
 //   2. R and gamma QS for every node into LDS: on matrix cores for bf16 with
 //      d_k = d_v = 128 (32x32x16 bf16, S split into hi + lo words; the S block
 //      and the first node tile are loaded before step 1, so their HBM latency
@@ -34,11 +34,14 @@
 //   3. per chunk: path walk (entry nodes and decays), Gram dot products by
 //      one 8-lane group per node, four of its entries in flight at a time
 //      (the ancestor-masked Gram/decay builder), level solve, outputs (U and
-//      o stored to HBM once).
+//      o stored to HBM once).  When the whole tree's entries fit in LDS (up
+//      to 4608 with bf16 inputs, 1400 with fp32) the walk and the Gram
+//      values are computed for the first column block only and reused.
 //
 // One workgroup fills most of a CU's LDS (R/U and gamma QS for 512 nodes x 32
-// columns are 128 KB), so a CU runs one at a time and latency is hidden inside
-// the workgroup: eight waves, loads issued ahead of use.
+// columns are 96 KB with bf16 gamma QS), so a CU runs one at a time and
+// latency is hidden inside the workgroup: sixteen waves, loads issued ahead of
+// use.
 #include "tv_device.h"
 #include "tv_launch.h"
 
@@ -47,22 +50,30 @@ namespace tv {
 namespace {
 
 constexpr int kBT = 1024;   // threads per workgroup (16 waves: one node tile each)
-constexpr int kBVB = 32;    // value columns per workgroup (d_v when d_v < 32)
-constexpr int kBEnt = 1400; // path entries per chunk (what LDS has room for)
+constexpr int kBVB = 32;    // value columns per pass (d_v when d_v < 32)
 constexpr int kBD = 128;    // d_k = d_v of the matrix-core contraction
+
+// Path entries LDS has room for: gamma QS is kept in the input type (bf16 o
+// is rounded to it anyway), which leaves more room with bf16 inputs.
+template <typename TIn>
+constexpr int blocked_entries() { return sizeof(TIn) == 2 ? 3040 : 1400; }
 
 typedef __bf16 bbf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bbf16x2 __attribute__((ext_vector_type(2)));
 typedef float bf32x16 __attribute__((ext_vector_type(16)));
 
+template <typename TIn>
 struct BlockedLds {
+  static constexpr int kEnt = blocked_entries<TIn>();
   float U[kMaxTree * kBVB];   // R rows, solved in place into U rows (row stride = columns)
-  float QS[kMaxTree * kBVB];  // gamma_n QS_n rows
-  float cA[kBEnt];            // decay during the walk, then beta_n D (k_n.k_j)
-  float cP[kBEnt];            // D (q_n.k_j)
-  uint16_t en[kBEnt];         // the entry's path node j
+  TIn QS[kMaxTree * kBVB];    // gamma_n QS_n rows, in the input type
+  float Sst[sizeof(TIn) == 2 ? kBD * kBVB : 1];  // S block of the matrix-core path
+  float cA[kEnt];             // decay during the walk, then A = beta_n D (k_n.k_j) (1 on
+                              // the node's own entry), then T = (I + A)^-1 if resident
+  float cP[kEnt];             // D (q_n.k_j), then the output weights of R if resident
+  uint16_t en[kEnt];          // the entry's path node j
   int16_t par[kMaxTree];
-  int16_t jmp[kMaxTree];
+  int16_t jmp[kMaxTree];      // jump targets, then node -> position
   int16_t len[kMaxTree];      // path length = depth + 1
   int16_t ord[kMaxTree];      // position -> node, positions sorted by depth
   int off[kMaxTree + 1];      // position -> first entry; off[N] = all entries
@@ -123,24 +134,59 @@ struct TileIn {
   uint2 vv[4];
 };
 
-__device__ __forceinline__ void load_tile(TileIn& t, int T, int N, int H, int b, int h, int c0,
-                                          bool gdn, const uint16_t* __restrict__ q,
-                                          const uint16_t* __restrict__ k,
-                                          const uint16_t* __restrict__ v) {
-  const int lane = threadIdx.x & 63;
-  const int lm = lane & 31, hi = lane >> 5;
-  const int n = T * 32 + lm;
-  const size_t row = ((size_t)b * N + (n < N ? n : N - 1)) * H + h;
-  const uint16_t* qr = q + row * kBD + 8 * hi;
-  const uint16_t* kr = k + row * kBD + 8 * hi;
+// Lane offsets of a tile row.  The lane index is made opaque so the offsets
+// are recomputed at every call (a few ALU ops) instead of being hoisted out of
+// the column block loop and held, or spilled, across it.  Uniform bases go in
+// scalar registers and offsets are 32-bit bytes (the launch checks that a
+// sequence's N H 128 bf16 elements fit in them).
+//
+// The loads are issued unconditionally (branches around them make the
+// compiler wait for the whole batch at the join): a wave with no tile, or a
+// load with nothing to fetch, reads the base row in every lane, one line.
+__device__ __forceinline__ uint32_t tile_rowoff(int T, int N, int H, bool real, int& hi) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  hi = lane >> 5;
+  const int n = T * 32 + (lane & 31);
+  return real ? static_cast<uint32_t>((n < N ? n : N - 1) * H * kBD) * 2u : 0u;
+}
+
+// q and k of tile T: element 8 (lane/32) + 16 ks of row T*32 + lane%32
+__device__ __forceinline__ void load_tile_qk(TileIn& t, int T, int N, int H, int b, int h, bool gdn,
+                                             bool real, const uint16_t* __restrict__ q,
+                                             const uint16_t* __restrict__ k) {
+  int hi;
+  const uint32_t off = tile_rowoff(T, N, H, real, hi) + 16u * hi;
+  const size_t base = ((size_t)b * N * H + h) * kBD;
+  const char* qr = reinterpret_cast<const char*>(q + base) + off;
+  // branch-free: without the delta rule the k operand is unused and these
+  // loads re-read the q rows just fetched
+  const char* kr = reinterpret_cast<const char*>((gdn ? k : q) + base) + off;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    t.qb[ks] = *reinterpret_cast<const bbf16x8*>(qr + 16 * ks);
-    if (gdn) t.kb[ks] = *reinterpret_cast<const bbf16x8*>(kr + 16 * ks);
+    t.qb[ks] = *reinterpret_cast<const bbf16x8*>(qr + 32 * ks);
+    t.kb[ks] = *reinterpret_cast<const bbf16x8*>(kr + 32 * ks);
   }
+}
+
+// v of tile T at the accumulator's columns: c0 + 8 g + 4 (lane/32) + [0, 4)
+__device__ __forceinline__ void load_tile_v(TileIn& t, int T, int N, int H, int b, int h, int c0,
+                                            bool real, const uint16_t* __restrict__ v) {
+  int hi;
+  const uint32_t off = tile_rowoff(T, N, H, real, hi) + 8u * hi;
+  const char* vr = reinterpret_cast<const char*>(v + ((size_t)b * N * H + h) * kBD + c0) + off;
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
-    t.vv[g] = *reinterpret_cast<const uint2*>(v + row * kBD + c0 + 8 * g + 4 * hi);
+  for (int g = 0; g < 4; ++g) t.vv[g] = *reinterpret_cast<const uint2*>(vr + 16 * g);
+}
+
+// This thread's float4 of a 128 x 32 S block (row tid/8, columns 4 (tid%8) +
+// [0, 4)); the lane offset is opaque so that no 64-bit address is held
+// across the phases between two blocks.
+__device__ __forceinline__ float4 load_s_part(const float* __restrict__ blk) {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  const uint32_t off = static_cast<uint32_t>(((t >> 3) * kBD + 4 * (t & 7)) * 4);
+  return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(blk) + off);
 }
 
 // [K;Q] S_block products of one tile.  A = S block^T (value column x d_k),
@@ -178,7 +224,7 @@ __device__ __forceinline__ void mma_tile(const TileIn& t, const float* Sst, bool
 
 // R and gamma QS of one tile into LDS: the accumulator puts node lane%32 and
 // value columns 8 (r/4) + 4 (lane/32) + r%4 in lane `lane`.
-__device__ __forceinline__ void store_tile(BlockedLds& s, const TileIn& t, int T, int N, bool gdn,
+__device__ __forceinline__ void store_tile(BlockedLds<uint16_t>& s, const TileIn& t, int T, int N, bool gdn,
                                            const bf32x16& kacc, const bf32x16& qacc) {
   const int lane = threadIdx.x & 63;
   const int n = T * 32 + (lane & 31);
@@ -198,15 +244,15 @@ __device__ __forceinline__ void store_tile(BlockedLds& s, const TileIn& t, int T
     }
     const int col = 8 * g + 4 * (lane >> 5);
     *reinterpret_cast<float4*>(&s.U[urow(n, col, kBVB)]) = r;
-    *reinterpret_cast<float4*>(&s.QS[urow(n, col, kBVB)]) =
-        make_float4(gn * qacc[4 * g + 0], gn * qacc[4 * g + 1], gn * qacc[4 * g + 2],
-                    gn * qacc[4 * g + 3]);
+    Elem<uint16_t>::store4(s.QS, urow(n, col, kBVB),
+                           make_float4(gn * qacc[4 * g + 0], gn * qacc[4 * g + 1],
+                                       gn * qacc[4 * g + 2], gn * qacc[4 * g + 3]));
   }
 }
 
 // The same with fp32 FMA, any d_k, d_v and input type; item = (node, 4 columns).
 template <typename TIn>
-__device__ void contract_fma(BlockedLds& s, int N, int H, int dk, int dv, int vb, int b, int h,
+__device__ void contract_fma(BlockedLds<TIn>& s, int N, int H, int dk, int dv, int vb, int b, int h,
                              int bh, int c0, bool gdn, const TIn* __restrict__ q,
                              const TIn* __restrict__ k, const TIn* __restrict__ v,
                              const float* __restrict__ S_root) {
@@ -226,7 +272,271 @@ __device__ void contract_fma(BlockedLds& s, int N, int H, int dk, int dv, int vb
     float4 r = Elem<TIn>::load4(v, row * dv + c0 + col);
     if (gdn) r = mul4(s.bet[n], sub4(r, mul4(gn, ks)));
     *reinterpret_cast<float4*>(&s.U[urow(n, col, vb)]) = r;
-    *reinterpret_cast<float4*>(&s.QS[urow(n, col, vb)]) = mul4(gn, qs);
+    Elem<TIn>::store4(s.QS, urow(n, col, vb), mul4(gn, qs));
+  }
+}
+
+// ---- per-chunk phases: positions [p0, p1) of the depth order, their path
+// entries stored from entry e0 on ----
+
+// Last position + 1 of the chunk that starts at p0: as many nodes as have all
+// their entries within kEnt of e0 (a node has at most 512 entries, so at
+// least one node fits).
+template <typename TIn>
+__device__ __forceinline__ int chunk_end(BlockedLds<TIn>& s, int p0, int N) {
+  const int e0 = s.off[p0];
+  const int qpos = p0 + 1 + threadIdx.x;
+  return p0 + __syncthreads_count(qpos <= N && s.off[qpos] - e0 <= BlockedLds<TIn>::kEnt);
+}
+
+// Path walk: entry t of node n is (n, e_t) with decay D(e_t -> n).
+template <typename TIn>
+__device__ __forceinline__ void walk_entries(BlockedLds<TIn>& s, int p0, int p1, int e0) {
+  for (int p = p0 + threadIdx.x; p < p1; p += kBT) {
+    const int n = s.ord[p];
+    int x = s.off[p] - e0;
+    float D = 1.f;
+    for (int e = n; e >= 0; e = s.par[e]) {
+      s.en[x] = static_cast<uint16_t>(e);
+      s.cA[x] = D;
+      D *= s.alp[e];
+      ++x;
+    }
+  }
+}
+
+// Gram values of the entries: cP = D (q_n.k_j), cA = beta_n D (k_n.k_j) (0 for
+// the node's own entry).  One 8-lane group per node, its q and k rows loaded
+// once, its entries four at a time.
+template <typename TIn, bool MFMA>
+__device__ __forceinline__ void gram_entries(BlockedLds<TIn>& s, int p0, int p1, int e0, int N,
+                                             int H, int dk, int b, int h, bool gdn,
+                                             const TIn* __restrict__ q,
+                                             const TIn* __restrict__ k) {
+  const int grp = threadIdx.x >> 3, lj = threadIdx.x & 7;
+  constexpr int kGroups = kBT / 8;
+  for (int p = p0 + grp; p < p1; p += kGroups) {
+    const int n = s.ord[p];
+    const int x0 = s.off[p] - e0;
+    const int L = s.len[n];
+    const float bn = s.bet[n];
+    const size_t rn = ((size_t)b * N + n) * H + h;
+    if constexpr (MFMA) {
+      // bf16, d_k = 128: lane lj covers elements [16 lj, 16 lj + 16)
+      const uint4* qn = reinterpret_cast<const uint4*>(q + rn * kBD) + 2 * lj;
+      const uint4* kn = reinterpret_cast<const uint4*>(k + rn * kBD) + 2 * lj;
+      const uint4 qa0 = qn[0], qa1 = qn[1];
+      uint4 ka0 = make_uint4(0, 0, 0, 0), ka1 = ka0;
+      if (gdn) {
+        ka0 = kn[0];
+        ka1 = kn[1];
+      }
+      for (int t0 = 0; t0 < L; t0 += 4) {
+        uint4 ea[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = t0 + u < L ? s.en[x0 + t0 + u] : n;
+          const uint4* ke = reinterpret_cast<const uint4*>(k + (((size_t)b * N + e) * H + h) * kBD) + 2 * lj;
+          ea[u][0] = ke[0];
+          ea[u][1] = ke[1];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float sq = dpp_sum8(dot8_bf16(qa1, ea[u][1], dot8_bf16(qa0, ea[u][0], 0.f)));
+          const float sk =
+              gdn ? dpp_sum8(dot8_bf16(ka1, ea[u][1], dot8_bf16(ka0, ea[u][0], 0.f))) : 0.f;
+          const int x = x0 + t0 + u;
+          if (lj == 0 && t0 + u < L) {
+            const float D = s.cA[x];
+            s.cP[x] = D * sq;
+            s.cA[x] = t0 + u > 0 ? bn * D * sk : 1.f;
+          }
+        }
+      }
+    } else {
+      for (int t = 0; t < L; ++t) {
+        const int e = s.en[x0 + t];
+        const size_t re = ((size_t)b * N + e) * H + h;
+        float a = 0.f, c = 0.f;
+        for (int i = lj; i < dk; i += 8) {
+          const float ke = Elem<TIn>::load(k, re * dk + i);
+          a = fmaf(Elem<TIn>::load(q, rn * dk + i), ke, a);
+          if (gdn) c = fmaf(Elem<TIn>::load(k, rn * dk + i), ke, c);
+        }
+        const float sq = dpp_sum8(a);
+        const float sk = dpp_sum8(c);
+        if (lj == 0) {
+          const float D = s.cA[x0 + t];
+          s.cP[x0 + t] = D * sq;
+          s.cA[x0 + t] = t > 0 ? bn * D * sk : 1.f;
+        }
+      }
+    }
+  }
+}
+
+// Level solve u_n = R_n - sum_{t >= 1} A[n, e_t] u_{e_t}, one depth level at a
+// time (a barrier after each); the chunk's lower levels were solved before.
+template <typename TIn>
+__device__ __forceinline__ void level_solve(BlockedLds<TIn>& s, int p0, int p1, int e0, int vb) {
+  const int ncg = vb / 4;
+  const int dlo = s.len[s.ord[p0]] - 1;
+  const int dhi = s.len[s.ord[p1 - 1]] - 1;
+  for (int l = dlo > 1 ? dlo : 1; l <= dhi; ++l) {
+    const int a = p0 > s.lst[l] ? p0 : s.lst[l];
+    const int z = p1 < s.lst[l + 1] ? p1 : s.lst[l + 1];
+    for (int it = threadIdx.x; it < (z - a) * ncg; it += kBT) {
+      const int p = a + it / ncg;
+      const int col = 4 * (it % ncg);
+      const int n = s.ord[p];
+      const int x = s.off[p] - e0;
+      float4 u = *reinterpret_cast<const float4*>(&s.U[urow(n, col, vb)]);
+#pragma unroll 4
+      for (int t = 1; t <= l; ++t) {
+        const float c = s.cA[x + t];
+        const float4 w = *reinterpret_cast<const float4*>(&s.U[urow(s.en[x + t], col, vb)]);
+        u.x = fmaf(-c, w.x, u.x);
+        u.y = fmaf(-c, w.y, u.y);
+        u.z = fmaf(-c, w.z, u.z);
+        u.w = fmaf(-c, w.w, u.w);
+      }
+      *reinterpret_cast<float4*>(&s.U[urow(n, col, vb)]) = u;
+    }
+    __syncthreads();
+  }
+}
+
+// Outputs of the chunk's nodes for value columns [c0, c0 + vb): o_n =
+// gamma_n QS_n + sum_t cP u_{e_t}, and the U rows, each stored to HBM once.
+template <typename TIn>
+__device__ __forceinline__ void chunk_outputs(BlockedLds<TIn>& s, int p0, int p1, int e0, int vb,
+                                              int N, int H, int dv, int b, int h, int bh, int c0,
+                                              TIn* __restrict__ o, float* __restrict__ U) {
+  const int ncg = vb / 4;
+  for (int it = threadIdx.x; it < (p1 - p0) * ncg; it += kBT) {
+    const int p = p0 + it / ncg;
+    const int col = 4 * (it % ncg);
+    const int n = s.ord[p];
+    const int x = s.off[p] - e0;
+    const int L = s.len[n];
+    float4 acc = Elem<TIn>::load4(s.QS, urow(n, col, vb));
+#pragma unroll 4
+    for (int t = 0; t < L; ++t) {
+      const float c = s.cP[x + t];
+      const float4 w = *reinterpret_cast<const float4*>(&s.U[urow(s.en[x + t], col, vb)]);
+      acc = fma4(c, w, acc);
+    }
+    Elem<TIn>::store4(o, (((size_t)b * N + n) * H + h) * dv + c0 + col, acc);
+    *reinterpret_cast<float4*>(U + ((size_t)bh * N + n) * dv + c0 + col) =
+        *reinterpret_cast<const float4*>(&s.U[urow(n, col, vb)]);
+  }
+}
+
+// ---- resident trees: the solve as a product with the inverse ----
+//
+// T = (I + A)^-1 is supported on root paths like A (products of path-supported
+// matrices stay path-supported), so U = T R needs, per node, only its own
+// path entries: u_n = sum_s T[n, e_s] R_{e_s}.  From T = I - A T, entry s of
+// node n's row is
+//   T[n, e_s] = - sum_{t=1..s} A[n, e_t] T[e_t, e_s],
+// where T[e_t, e_s] is entry s - t of ancestor e_t's row (1 when t = s).  Rows
+// are computed one depth level at a time, in place of A: each value is held
+// in a register until the level's reads are done.  The outputs then fold in T
+// the same way, o_n = gamma_n QS_n + sum_s W[n, e_s] R_{e_s} with
+//   W[n, e_s] = sum_{t=0..s} Pc[n, e_t] T[e_t, e_s],   Pc[n, j] = D(j->n) (q_n.k_j),
+// in place of Pc.  Both are scalar work per path entry, done once for all
+// column blocks; each block is then one gather over R rows with no levels.
+constexpr int kItemsPerThread = 3;  // path entries per thread (kEnt <= 3 kBT)
+
+template <typename TIn>
+__device__ __forceinline__ void tree_inverse(BlockedLds<TIn>& s, int N) {
+  static_assert(BlockedLds<TIn>::kEnt <= kItemsPerThread * kBT, "entries per thread");
+  const int maxd = s.len[s.ord[N - 1]] - 1;
+  for (int l = 1; l <= maxd; ++l) {
+    const int a = s.lst[l];
+    const int items = (s.lst[l + 1] - a) * l;  // entries s = 1..l of the level's nodes
+    float val[kItemsPerThread];
+    int dst[kItemsPerThread];
+#pragma unroll
+    for (int r = 0; r < kItemsPerThread; ++r) {
+      const int it = threadIdx.x + r * kBT;
+      dst[r] = -1;
+      val[r] = 0.f;
+      if (it < items) {
+        const int p = a + it / l;
+        const int sp = 1 + it % l;
+        const int x = s.off[p];
+        float acc = 0.f;
+        for (int t = 1; t <= sp; ++t) {
+          const int xe = s.off[s.jmp[s.en[x + t]]];  // ancestor e_t's row
+          acc = fmaf(s.cA[x + t], s.cA[xe + sp - t], acc);
+        }
+        val[r] = -acc;
+        dst[r] = x + sp;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kItemsPerThread; ++r)
+      if (dst[r] >= 0) s.cA[dst[r]] = val[r];
+    __syncthreads();
+  }
+  // output weights of every entry (all T rows are final)
+  const int nent = s.off[N];
+  float val[kItemsPerThread];
+#pragma unroll
+  for (int r = 0; r < kItemsPerThread; ++r) {
+    const int x = threadIdx.x + r * kBT;
+    val[r] = 0.f;
+    if (x < nent) {
+      int d = 0;
+      while (s.ebase[d + 1] <= x) ++d;  // the entry's depth: rows of length d + 1
+      const int sp = (x - s.ebase[d]) % (d + 1);
+      const int xn = x - sp;             // node n's row
+      float acc = 0.f;
+      for (int t = 0; t <= sp; ++t) {
+        const int xe = t == 0 ? xn : s.off[s.jmp[s.en[xn + t]]];
+        acc = fmaf(s.cP[xn + t], s.cA[xe + sp - t], acc);
+      }
+      val[r] = acc;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kItemsPerThread; ++r) {
+    const int x = threadIdx.x + r * kBT;
+    if (x < nent) s.cP[x] = val[r];
+  }
+  __syncthreads();
+}
+
+// u_n and o_n of every node for value columns [c0, c0 + vb) from the R rows
+// (left unchanged in LDS) and the entries' T and output weights.
+template <typename TIn>
+__device__ __forceinline__ void gather_outputs(BlockedLds<TIn>& s, int vb, int N, int H, int dv,
+                                               int b, int h, int bh, int c0,
+                                               TIn* __restrict__ o, float* __restrict__ U) {
+  const int ncg = vb / 4;
+  // positions are sorted by depth, so rounds alternate the lane order: each
+  // wave gets shallow and deep nodes alike
+  for (int r = 0; r * kBT < N * ncg; ++r) {
+    const int it = r * kBT + ((r & 1) ? kBT - 1 - (int)threadIdx.x : (int)threadIdx.x);
+    if (it >= N * ncg) continue;
+    const int p = it / ncg;
+    const int col = 4 * (it % ncg);
+    const int n = s.ord[p];
+    const int x = s.off[p];
+    const int L = s.len[n];
+    float4 acc = Elem<TIn>::load4(s.QS, urow(n, col, vb));
+    float4 u = f4(0.f);
+#pragma unroll 4
+    for (int t = 0; t < L; ++t) {
+      const float4 w = *reinterpret_cast<const float4*>(&s.U[urow(s.en[x + t], col, vb)]);
+      acc = fma4(s.cP[x + t], w, acc);
+      u = fma4(s.cA[x + t], w, u);
+    }
+    Elem<TIn>::store4(o, (((size_t)b * N + n) * H + h) * dv + c0 + col, acc);
+    *reinterpret_cast<float4*>(U + ((size_t)bh * N + n) * dv + c0 + col) = u;
   }
 }
 
@@ -236,17 +546,15 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     const TIn* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
     const int32_t* __restrict__ parents, const float* __restrict__ S_root, TIn* __restrict__ o,
     float* __restrict__ U, int32_t* __restrict__ status) {
-  __shared__ BlockedLds s;
+  __shared__ BlockedLds<TIn> s;
+  constexpr int kEnt = BlockedLds<TIn>::kEnt;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int vb = dv < kBVB ? dv : kBVB;
   const int nvb = dv / vb;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int cb = bid % nvb;
-  const int bh = bid / nvb;
+  const int bh = xcd_remap(blockIdx.x, gridDim.x);
   const int h = bh % H;
   const int b = bh / H;
-  const int c0 = cb * vb;
   const bool gdn = mode == kGdn;
   const int ntiles = (N + 31) / 32;
 
@@ -256,19 +564,43 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
   const float a_in = alpha[((size_t)b * N + pn) * H + h];
   const float b_in = gdn ? beta[((size_t)b * N + pn) * H + h] : 0.f;
 
-  // matrix-core path: the S block (128 x 32 fp32, 16 KB) staged once in LDS by
-  // coalesced loads (in the U rows, unused until the contraction's results),
-  // and the wave's first node tile, both in flight during the tree build
+  // matrix-core path: a column block's S block (128 x 32 fp32, 16 KB, one
+  // float4 per thread) and the wave's node tile are loaded into registers one
+  // phase ahead of their use; those of the first block are in flight during
+  // the tree build
+  static_assert(kBT * 4 == kBD * kBVB, "one float4 of the S block per thread");
+  static_assert(kMaxTree / 32 <= kBT / 64, "a node tile per wave");
   TileIn t0;
-  if constexpr (MFMA) {
-    float4* Sl = reinterpret_cast<float4*>(s.U);
-    const float* Sb = S_root + (size_t)bh * kBD * kBD + c0;
-    static_assert(kBT * 4 == kBD * kBVB, "one float4 of the S block per thread");
-    Sl[tid] = *reinterpret_cast<const float4*>(Sb + (size_t)(tid >> 3) * kBD + 4 * (tid & 7));
-    if (wave < ntiles)
-      load_tile(t0, wave, N, H, b, h, c0, gdn, reinterpret_cast<const uint16_t*>(q),
-                reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v));
+  float4 snext;
+// (straight-line: without a load to do, the first block's S rows or one line
+// per wave are read); v, which only the contraction's last step needs, is
+// loaded later
+#define TV_LOAD_S(c0, load)                                                                \
+  if constexpr (MFMA) snext = load_s_part(S_root + (size_t)bh * kBD * kBD + ((load) ? (c0) : 0));
+#define TV_LOAD_QK(load)                                                                   \
+  if constexpr (MFMA) {                                                                    \
+    load_tile_qk(t0, wave, N, H, b, h, gdn, (load) && wave < ntiles,                       \
+                 reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k)); \
   }
+#define TV_LOAD_V(c0, load)                                                                \
+  if constexpr (MFMA) {                                                                    \
+    const bool ld_ = (load);                                                               \
+    load_tile_v(t0, wave, N, H, b, h, ld_ ? (c0) : 0, ld_ && wave < ntiles,                \
+                reinterpret_cast<const uint16_t*>(v));                                     \
+  }
+  // R and gamma QS of every node for columns [c0, c0 + vb) into LDS (the S
+  // block already staged)
+#define TV_CONTRACT(c0)                                                                    \
+  if constexpr (MFMA) {                                                                    \
+    if (wave < ntiles) {                                                                   \
+      bf32x16 kacc, qacc;                                                                  \
+      mma_tile(t0, s.Sst, gdn, kacc, qacc);                                                \
+      store_tile(s, t0, wave, N, gdn, kacc, qacc);                                         \
+    }                                                                                      \
+  } else {                                                                                 \
+    contract_fma<TIn>(s, N, H, dk, dv, vb, b, h, bh, (c0), gdn, q, k, v, S_root);          \
+  }
+  TV_LOAD_S(0, true)
 
   // ---- 1. tree index ----
   if (tid == 0) s.maxd = 0;
@@ -329,161 +661,78 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
   if (tid < N) {
     const int pos = s.lst[my_d] + atomicSub(&s.hist[my_d], 1) - 1;
     s.ord[pos] = static_cast<int16_t>(tid);
+    s.jmp[tid] = static_cast<int16_t>(pos);  // pointer jumping is over
     s.off[pos] = s.ebase[my_d] + (pos - s.lst[my_d]) * (my_d + 1);
   }
   if (tid == 0) s.off[N] = s.ebase[maxd + 1];
-  if (h == 0 && cb == 0 && tid == 0 && status) status[b] = bad ? 1 : 0;
+  if (h == 0 && tid == 0 && status) status[b] = bad ? 1 : 0;
+  if constexpr (MFMA) reinterpret_cast<float4*>(s.Sst)[tid] = snext;
   __syncthreads();
 
-  // ---- 2. R and gamma QS ----
-  if constexpr (MFMA) {
-    // one node tile per wave (N <= 512 is at most 16 tiles); the S block sits
-    // in the U rows until every wave has its products
-    static_assert(kMaxTree / 32 <= kBT / 64, "a node tile per wave");
-    bf32x16 kacc, qacc;
-    if (wave < ntiles) mma_tile(t0, s.U, gdn, kacc, qacc);
+  // Chunks of path entries, as many as LDS holds.  When the whole tree's
+  // entries fit (one chunk), they are walked, given their Gram values and
+  // turned into T and output weights once, and each column block is one
+  // gather; otherwise every block walks its chunks again and solves them
+  // level by level.  The last chunk of a block is peeled out of the chunk
+  // loop: the next block's S block and node tile load during its solve and
+  // outputs.
+  const bool resident = s.off[N] <= kEnt;
+  if (resident) {
+    // the first block's node tiles load during the inverse (not before: every
+    // workgroup would fetch them at once and the tree build would wait)
+    walk_entries(s, 0, N, 0);
     __syncthreads();
-    if (wave < ntiles) store_tile(s, t0, wave, N, gdn, kacc, qacc);
+    gram_entries<TIn, MFMA>(s, 0, N, 0, N, H, dk, b, h, gdn, q, k);
+    __syncthreads();
+    TV_LOAD_QK(true)
+    TV_LOAD_V(0, true)
+    if (gdn) tree_inverse(s, N);
   } else {
-    contract_fma<TIn>(s, N, H, dk, dv, vb, b, h, bh, c0, gdn, q, k, v, S_root);
+    TV_LOAD_QK(true)
+    TV_LOAD_V(0, true)
   }
-  __syncthreads();
-
-  // ---- 3. chunks of path entries ----
-  const int ncg = vb / 4;
-  const int grp = tid >> 3, lj = tid & 7;
-  constexpr int kGroups = kBT / 8;
-  for (int p0 = 0; p0 < N;) {
-    const int e0 = s.off[p0];
-    const int qpos = p0 + 1 + tid;
-    const int p1 = p0 + __syncthreads_count(qpos <= N && s.off[qpos] - e0 <= kBEnt);
-    const int nent = s.off[p1] - e0;
-
-    // path walk: entry t of node n is (n, e_t) with decay D(e_t -> n)
-    for (int p = p0 + tid; p < p1; p += kBT) {
-      const int n = s.ord[p];
-      int x = s.off[p] - e0;
-      float D = 1.f;
-      for (int e = n; e >= 0; e = s.par[e]) {
-        s.en[x] = static_cast<uint16_t>(e);
-        s.cA[x] = D;
-        D *= s.alp[e];
-        ++x;
-      }
-    }
-    __syncthreads();
-
-    // Gram values of the entries: one 8-lane group per node (its q and k rows
-    // loaded once), its entries four at a time
-    for (int p = p0 + grp; p < p1; p += kGroups) {
-      const int n = s.ord[p];
-      const int x0 = s.off[p] - e0;
-      const int L = s.len[n];
-      const float bn = s.bet[n];
-      const size_t rn = ((size_t)b * N + n) * H + h;
-      if constexpr (MFMA) {
-        // bf16, d_k = 128: lane lj covers elements [16 lj, 16 lj + 16)
-        const uint4* qn = reinterpret_cast<const uint4*>(q + rn * kBD) + 2 * lj;
-        const uint4* kn = reinterpret_cast<const uint4*>(k + rn * kBD) + 2 * lj;
-        const uint4 qa0 = qn[0], qa1 = qn[1];
-        uint4 ka0 = make_uint4(0, 0, 0, 0), ka1 = ka0;
-        if (gdn) {
-          ka0 = kn[0];
-          ka1 = kn[1];
-        }
-        for (int t0 = 0; t0 < L; t0 += 4) {
-          uint4 ea[4][2];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int e = t0 + u < L ? s.en[x0 + t0 + u] : n;
-            const uint4* ke = reinterpret_cast<const uint4*>(k + (((size_t)b * N + e) * H + h) * kBD) + 2 * lj;
-            ea[u][0] = ke[0];
-            ea[u][1] = ke[1];
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float sq = dpp_sum8(dot8_bf16(qa1, ea[u][1], dot8_bf16(qa0, ea[u][0], 0.f)));
-            const float sk =
-                gdn ? dpp_sum8(dot8_bf16(ka1, ea[u][1], dot8_bf16(ka0, ea[u][0], 0.f))) : 0.f;
-            const int x = x0 + t0 + u;
-            if (lj == 0 && t0 + u < L) {
-              const float D = s.cA[x];
-              s.cP[x] = D * sq;
-              s.cA[x] = t0 + u > 0 ? bn * D * sk : 0.f;
-            }
-          }
-        }
-      } else {
-        for (int t = 0; t < L; ++t) {
-          const int e = s.en[x0 + t];
-          const size_t re = ((size_t)b * N + e) * H + h;
-          float a = 0.f, c = 0.f;
-          for (int i = lj; i < dk; i += 8) {
-            const float ke = Elem<TIn>::load(k, re * dk + i);
-            a = fmaf(Elem<TIn>::load(q, rn * dk + i), ke, a);
-            if (gdn) c = fmaf(Elem<TIn>::load(k, rn * dk + i), ke, c);
-          }
-          const float sq = dpp_sum8(a);
-          const float sk = dpp_sum8(c);
-          if (lj == 0) {
-            const float D = s.cA[x0 + t];
-            s.cP[x0 + t] = D * sq;
-            s.cA[x0 + t] = t > 0 ? bn * D * sk : 0.f;
-          }
-        }
-      }
-    }
-    __syncthreads();
-
-    // level solve: u_n = R_n - sum_{t >= 1} A[n, e_t] u_{e_t}
-    if (gdn) {
-      const int dlo = s.len[s.ord[p0]] - 1;
-      const int dhi = s.len[s.ord[p1 - 1]] - 1;
-      for (int l = dlo > 1 ? dlo : 1; l <= dhi; ++l) {
-        const int a = p0 > s.lst[l] ? p0 : s.lst[l];
-        const int z = p1 < s.lst[l + 1] ? p1 : s.lst[l + 1];
-        for (int it = tid; it < (z - a) * ncg; it += kBT) {
-          const int p = a + it / ncg;
-          const int col = 4 * (it % ncg);
-          const int n = s.ord[p];
-          const int x = s.off[p] - e0;
-          float4 u = *reinterpret_cast<const float4*>(&s.U[urow(n, col, vb)]);
-#pragma unroll 4
-          for (int t = 1; t <= l; ++t) {
-            const float c = s.cA[x + t];
-            const float4 w = *reinterpret_cast<const float4*>(&s.U[urow(s.en[x + t], col, vb)]);
-            u.x = fmaf(-c, w.x, u.x);
-            u.y = fmaf(-c, w.y, u.y);
-            u.z = fmaf(-c, w.z, u.z);
-            u.w = fmaf(-c, w.w, u.w);
-          }
-          *reinterpret_cast<float4*>(&s.U[urow(n, col, vb)]) = u;
-        }
+  TV_CONTRACT(0)
+  for (int cb = 0;;) {
+    const int c0 = cb * vb;
+    int p0 = 0, p1, e0;
+    while (true) {
+      e0 = s.off[p0];
+      p1 = chunk_end(s, p0, N);  // N at once when resident
+      if (!resident) {
+        walk_entries(s, p0, p1, e0);
         __syncthreads();
+        gram_entries<TIn, MFMA>(s, p0, p1, e0, N, H, dk, b, h, gdn, q, k);
       }
+      __syncthreads();
+      if (p1 == N) break;
+      if (gdn) level_solve(s, p0, p1, e0, vb);
+      chunk_outputs(s, p0, p1, e0, vb, N, H, dv, b, h, bh, c0, o, U);
+      __syncthreads();
+      p0 = p1;
     }
-
-    // outputs of the chunk's nodes
-    for (int it = tid; it < (p1 - p0) * ncg; it += kBT) {
-      const int p = p0 + it / ncg;
-      const int col = 4 * (it % ncg);
-      const int n = s.ord[p];
-      const int x = s.off[p] - e0;
-      const int L = s.len[n];
-      float4 acc = *reinterpret_cast<const float4*>(&s.QS[urow(n, col, vb)]);
-#pragma unroll 4
-      for (int t = 0; t < L; ++t) {
-        const float c = s.cP[x + t];
-        const float4 w = *reinterpret_cast<const float4*>(&s.U[urow(s.en[x + t], col, vb)]);
-        acc = fma4(c, w, acc);
-      }
-      Elem<TIn>::store4(o, (((size_t)b * N + n) * H + h) * dv + c0 + col, acc);
-      *reinterpret_cast<float4*>(U + ((size_t)bh * N + n) * dv + c0 + col) =
-          *reinterpret_cast<const float4*>(&s.U[urow(n, col, vb)]);
+    const bool more = cb + 1 < nvb;
+    TV_LOAD_S(c0 + vb, more)
+    TV_LOAD_QK(more)
+    if (resident) {
+      gather_outputs(s, vb, N, H, dv, b, h, bh, c0, o, U);
+    } else {
+      if (gdn) level_solve(s, p0, N, e0, vb);
+      chunk_outputs(s, p0, N, e0, vb, N, H, dv, b, h, bh, c0, o, U);
     }
+    if constexpr (MFMA) {
+      if (more) reinterpret_cast<float4*>(s.Sst)[tid] = snext;  // the block's products are done
+    }
+    TV_LOAD_V(c0 + vb, more)
     __syncthreads();
-    p0 = p1;
+    if (!more) break;
+    ++cb;
+    TV_CONTRACT(c0 + vb)
+    __syncthreads();
   }
+#undef TV_LOAD_S
+#undef TV_LOAD_QK
+#undef TV_LOAD_V
+#undef TV_CONTRACT
 }
 
 }  // namespace
@@ -492,11 +741,11 @@ int launch_verify_blocked(int B, int H, int N, int dk, int dv, int dtype, int mo
                           const void* k, const void* v, const float* alpha, const float* beta,
                           const int32_t* parents, const float* S_root, void* o, float* U,
                           int32_t* status, hipStream_t stream) {
-  const int vb = dv < kBVB ? dv : kBVB;
-  const long long nblocks = (long long)B * H * (dv / vb);
+  const long long nblocks = (long long)B * H;  // one workgroup per (sequence, head)
   if (nblocks > 0x7fffffffLL) return static_cast<int>(hipErrorInvalidConfiguration);
   const dim3 grid((unsigned)nblocks), block(kBT);
   if (dtype == 1 && dk == kBD && dv == kBD) {
+    if ((long long)N * H * kBD * 2 > 0xffffffffLL) return static_cast<int>(hipErrorInvalidValue);
     hipLaunchKernelGGL((verify_blocked_kernel<uint16_t, true>), grid, block, 0, stream, H, N, dk,
                        dv, mode, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), alpha, beta, parents, S_root,
