@@ -250,6 +250,79 @@ __device__ __forceinline__ void store_tile(BlockedLds<uint16_t>& s, const TileIn
   }
 }
 
+// The contraction for the register-resident path: R rows of the wave's tile
+// into LDS, gamma QS kept in the accumulator lanes as bf16 (the precision it
+// has in o), four value columns 8 g + 4 (lane/32) + [0, 4) per group g.
+__device__ __forceinline__ void contract_keep(BlockedLds<uint16_t>& s, const TileIn& t, int T,
+                                              int N, bool gdn, uint2 (&gq)[4]) {
+  bf32x16 kacc, qacc;
+  mma_tile(t, s.Sst, gdn, kacc, qacc);
+  const int lane = threadIdx.x & 63;
+  const int n = T * 32 + (lane & 31);
+  const bool live = n < N;
+  const int nn = live ? n : N - 1;
+  const float gn = s.gam[nn], bn = s.bet[nn];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint2 w = t.vv[g];
+    const float4 vf = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+    float4 r = vf;
+    if (gdn) {
+      r.x = bn * (vf.x - gn * kacc[4 * g + 0]);
+      r.y = bn * (vf.y - gn * kacc[4 * g + 1]);
+      r.z = bn * (vf.z - gn * kacc[4 * g + 2]);
+      r.w = bn * (vf.w - gn * kacc[4 * g + 3]);
+    }
+    if (live) *reinterpret_cast<float4*>(&s.U[urow(n, 8 * g + 4 * (lane >> 5), kBVB)]) = r;
+    gq[g].x = static_cast<uint32_t>(f32_to_bf16(gn * qacc[4 * g + 0])) |
+              (static_cast<uint32_t>(f32_to_bf16(gn * qacc[4 * g + 1])) << 16);
+    gq[g].y = static_cast<uint32_t>(f32_to_bf16(gn * qacc[4 * g + 2])) |
+              (static_cast<uint32_t>(f32_to_bf16(gn * qacc[4 * g + 3])) << 16);
+  }
+}
+
+// Outputs of the lane's own node n = 32 T + lane%32 at the columns whose
+// gamma QS it holds: o_n = gamma_n QS_n + sum_s W[n, e_s] R_{e_s} and u_n =
+// sum_s T[n, e_s] R_{e_s}, two column groups per pass over the entries.
+__device__ __forceinline__ void gather_owner(BlockedLds<uint16_t>& s, const uint2 (&gq)[4], int T,
+                                             int N, int H, int b, int h, int bh, int c0,
+                                             uint16_t* __restrict__ o, float* __restrict__ U) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // lane offsets computed here, not held across the block loop
+  const int n = T * 32 + (lane & 31), hi = lane >> 5;
+  if (n >= N) return;
+  const int x = s.off[s.jmp[n]];
+  const int L = s.len[n];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int ca = 16 * half + 4 * hi, cc = ca + 8;
+    const uint2 g0 = gq[2 * half], g1 = gq[2 * half + 1];
+    float4 a0 = make_float4(__uint_as_float(g0.x << 16), __uint_as_float(g0.x & 0xffff0000u),
+                            __uint_as_float(g0.y << 16), __uint_as_float(g0.y & 0xffff0000u));
+    float4 a1 = make_float4(__uint_as_float(g1.x << 16), __uint_as_float(g1.x & 0xffff0000u),
+                            __uint_as_float(g1.y << 16), __uint_as_float(g1.y & 0xffff0000u));
+    float4 u0 = f4(0.f), u1 = f4(0.f);
+#pragma unroll 2
+    for (int t = 0; t < L; ++t) {
+      const int e = s.en[x + t];
+      const float wt = s.cA[x + t], wp = s.cP[x + t];
+      const float4 r0 = *reinterpret_cast<const float4*>(&s.U[urow(e, ca, kBVB)]);
+      const float4 r1 = *reinterpret_cast<const float4*>(&s.U[urow(e, cc, kBVB)]);
+      a0 = fma4(wp, r0, a0);
+      a1 = fma4(wp, r1, a1);
+      u0 = fma4(wt, r0, u0);
+      u1 = fma4(wt, r1, u1);
+    }
+    const size_t orow = (((size_t)b * N + n) * H + h) * kBD + c0;
+    Elem<uint16_t>::store4(o, orow + ca, a0);
+    Elem<uint16_t>::store4(o, orow + cc, a1);
+    float* ur = U + ((size_t)bh * N + n) * kBD + c0;
+    *reinterpret_cast<float4*>(ur + ca) = u0;
+    *reinterpret_cast<float4*>(ur + cc) = u1;
+  }
+}
+
 // The same with fp32 FMA, any d_k, d_v and input type; item = (node, 4 columns).
 template <typename TIn>
 __device__ void contract_fma(BlockedLds<TIn>& s, int N, int H, int dk, int dv, int vb, int b, int h,
@@ -677,6 +750,36 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
   // loop: the next block's S block and node tile load during its solve and
   // outputs.
   const bool resident = s.off[N] <= kEnt;
+  if constexpr (MFMA) {
+    if (resident) {
+      // matrix-core path, entries resident: the q and k tiles are loaded once
+      // and stay in registers for every column block (no re-reads), gamma QS
+      // stays in the accumulator lanes, and each lane finishes the outputs of
+      // its own node
+      walk_entries(s, 0, N, 0);
+      __syncthreads();
+      gram_entries<TIn, MFMA>(s, 0, N, 0, N, H, dk, b, h, gdn, q, k);
+      __syncthreads();
+      TV_LOAD_QK(true)
+      TV_LOAD_V(0, true)
+      if (gdn) tree_inverse(s, N);
+      for (int cb = 0;;) {
+        const int c0 = cb * vb;
+        uint2 gq[4];
+        if (wave < ntiles) contract_keep(s, t0, wave, N, gdn, gq);
+        const bool more = cb + 1 < nvb;
+        TV_LOAD_S(c0 + vb, more)
+        TV_LOAD_V(c0 + vb, more)
+        __syncthreads();  // R rows in LDS
+        gather_owner(s, gq, wave, N, H, b, h, bh, c0, o, U);
+        if (more) reinterpret_cast<float4*>(s.Sst)[tid] = snext;  // the block's products are done
+        __syncthreads();
+        if (!more) break;
+        ++cb;
+      }
+      return;
+    }
+  }
   if (resident) {
     // the first block's node tiles load during the inverse (not before: every
     // workgroup would fetch them at once and the tree build would wait)
