@@ -134,29 +134,34 @@ struct TileIn {
   uint2 vv[4];
 };
 
-// Lane offsets of a tile row.  The lane index is made opaque so the offsets
-// are recomputed at every call (a few ALU ops) instead of being hoisted out of
-// the column block loop and held, or spilled, across it.  Uniform bases go in
-// scalar registers and offsets are 32-bit bytes (the launch checks that a
-// sequence's N H 128 bf16 elements fit in them).
+// Tile rows.  Lane l of a tile holds row (node) l%32 of the tile in the
+// matrix-core operand layout.  The node of a lane is passed in (-1: none);
+// it is made opaque so that the offsets derived from it are recomputed at
+// every call instead of being hoisted out of the column block loop and held,
+// or spilled, across it.  Uniform bases go in scalar registers and offsets are
+// 32-bit bytes (the launch checks that a sequence's N H 128 bf16 elements fit
+// in them).
 //
 // The loads are issued unconditionally (branches around them make the
-// compiler wait for the whole batch at the join): a wave with no tile, or a
-// load with nothing to fetch, reads the base row in every lane, one line.
-__device__ __forceinline__ uint32_t tile_rowoff(int T, int N, int H, bool real, int& hi) {
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));
-  hi = lane >> 5;
-  const int n = T * 32 + (lane & 31);
-  return real ? static_cast<uint32_t>((n < N ? n : N - 1) * H * kBD) * 2u : 0u;
+// compiler wait for the whole batch at the join): a lane with no row, or a
+// load with nothing to fetch, reads the base row, one line per wave.
+__device__ __forceinline__ uint32_t tile_rowoff(int node, int H) {
+  asm volatile("" : "+v"(node));
+  return node >= 0 ? static_cast<uint32_t>(node * H * kBD) * 2u : 0u;
 }
 
-// q and k of tile T: element 8 (lane/32) + 16 ks of row T*32 + lane%32
-__device__ __forceinline__ void load_tile_qk(TileIn& t, int T, int N, int H, int b, int h, bool gdn,
-                                             bool real, const uint16_t* __restrict__ q,
+// Identity mapping: tile T holds nodes 32 T .. 32 T + 31.
+__device__ __forceinline__ int identity_node(int T, int N) {
+  const int n = T * 32 + (threadIdx.x & 31);
+  return n < N ? n : -1;
+}
+
+// q and k of the lane's row: elements 8 (lane/32) + 16 ks
+__device__ __forceinline__ void load_tile_qk(TileIn& t, int node, int N, int H, int b, int h,
+                                             bool gdn, const uint16_t* __restrict__ q,
                                              const uint16_t* __restrict__ k) {
-  int hi;
-  const uint32_t off = tile_rowoff(T, N, H, real, hi) + 16u * hi;
+  const uint32_t hi = (threadIdx.x >> 5) & 1;
+  const uint32_t off = tile_rowoff(node, H) + 16u * hi;
   const size_t base = ((size_t)b * N * H + h) * kBD;
   const char* qr = reinterpret_cast<const char*>(q + base) + off;
   // branch-free: without the delta rule the k operand is unused and these
@@ -169,11 +174,11 @@ __device__ __forceinline__ void load_tile_qk(TileIn& t, int T, int N, int H, int
   }
 }
 
-// v of tile T at the accumulator's columns: c0 + 8 g + 4 (lane/32) + [0, 4)
-__device__ __forceinline__ void load_tile_v(TileIn& t, int T, int N, int H, int b, int h, int c0,
-                                            bool real, const uint16_t* __restrict__ v) {
-  int hi;
-  const uint32_t off = tile_rowoff(T, N, H, real, hi) + 8u * hi;
+// v of the lane's row at the accumulator's columns: c0 + 8 g + 4 (lane/32) + [0, 4)
+__device__ __forceinline__ void load_tile_v(TileIn& t, int node, int N, int H, int b, int h,
+                                            int c0, const uint16_t* __restrict__ v) {
+  const uint32_t hi = (threadIdx.x >> 5) & 1;
+  const uint32_t off = tile_rowoff(node, H) + 8u * hi;
   const char* vr = reinterpret_cast<const char*>(v + ((size_t)b * N * H + h) * kBD + c0) + off;
 #pragma unroll
   for (int g = 0; g < 4; ++g) t.vv[g] = *reinterpret_cast<const uint2*>(vr + 16 * g);
@@ -250,17 +255,18 @@ __device__ __forceinline__ void store_tile(BlockedLds<uint16_t>& s, const TileIn
   }
 }
 
-// The contraction for the register-resident path: R rows of the wave's tile
-// into LDS, gamma QS kept in the accumulator lanes as bf16 (the precision it
-// has in o), four value columns 8 g + 4 (lane/32) + [0, 4) per group g.
-__device__ __forceinline__ void contract_keep(BlockedLds<uint16_t>& s, const TileIn& t, int T,
-                                              int N, bool gdn, uint2 (&gq)[4]) {
+// The contraction for the register-resident path: R row of the lane's node
+// n (-1: none) into LDS, gamma QS kept in the accumulator lanes as bf16 (the
+// precision it has in o), four value columns 8 g + 4 (lane/32) + [0, 4) per
+// group g.  The matrix instructions run in every wave (rows without a node
+// hold the base row and are not stored).
+__device__ __forceinline__ void contract_keep(BlockedLds<uint16_t>& s, const TileIn& t, int n,
+                                              bool gdn, uint2 (&gq)[4]) {
   bf32x16 kacc, qacc;
   mma_tile(t, s.Sst, gdn, kacc, qacc);
   const int lane = threadIdx.x & 63;
-  const int n = T * 32 + (lane & 31);
-  const bool live = n < N;
-  const int nn = live ? n : N - 1;
+  const bool live = n >= 0;
+  const int nn = live ? n : 0;
   const float gn = s.gam[nn], bn = s.bet[nn];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -282,16 +288,15 @@ __device__ __forceinline__ void contract_keep(BlockedLds<uint16_t>& s, const Til
   }
 }
 
-// Outputs of the lane's own node n = 32 T + lane%32 at the columns whose
-// gamma QS it holds: o_n = gamma_n QS_n + sum_s W[n, e_s] R_{e_s} and u_n =
+// Outputs of the lane's own node n (-1: none) at the columns whose gamma QS
+// it holds: o_n = gamma_n QS_n + sum_s W[n, e_s] R_{e_s} and u_n =
 // sum_s T[n, e_s] R_{e_s}, two column groups per pass over the entries.
-__device__ __forceinline__ void gather_owner(BlockedLds<uint16_t>& s, const uint2 (&gq)[4], int T,
+__device__ __forceinline__ void gather_owner(BlockedLds<uint16_t>& s, const uint2 (&gq)[4], int n,
                                              int N, int H, int b, int h, int bh, int c0,
                                              uint16_t* __restrict__ o, float* __restrict__ U) {
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));  // lane offsets computed here, not held across the block loop
-  const int n = T * 32 + (lane & 31), hi = lane >> 5;
-  if (n >= N) return;
+  asm volatile("" : "+v"(n));  // offsets computed here, not held across the block loop
+  const int hi = (threadIdx.x >> 5) & 1;
+  if (n < 0) return;
   const int x = s.off[s.jmp[n]];
   const int L = s.len[n];
 #pragma unroll
@@ -650,15 +655,14 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
 // loaded later
 #define TV_LOAD_S(c0, load)                                                                \
   if constexpr (MFMA) snext = load_s_part(S_root + (size_t)bh * kBD * kBD + ((load) ? (c0) : 0));
-#define TV_LOAD_QK(load)                                                                   \
+#define TV_LOAD_QK(node, load)                                                             \
   if constexpr (MFMA) {                                                                    \
-    load_tile_qk(t0, wave, N, H, b, h, gdn, (load) && wave < ntiles,                       \
+    load_tile_qk(t0, (load) ? (node) : -1, N, H, b, h, gdn,                                \
                  reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k)); \
   }
-#define TV_LOAD_V(c0, load)                                                                \
+#define TV_LOAD_V(node, c0, load)                                                          \
   if constexpr (MFMA) {                                                                    \
-    const bool ld_ = (load);                                                               \
-    load_tile_v(t0, wave, N, H, b, h, ld_ ? (c0) : 0, ld_ && wave < ntiles,                \
+    load_tile_v(t0, (load) ? (node) : -1, N, H, b, h, (load) ? (c0) : 0,                   \
                 reinterpret_cast<const uint16_t*>(v));                                     \
   }
   // R and gamma QS of every node for columns [c0, c0 + vb) into LDS (the S
@@ -760,18 +764,23 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
       __syncthreads();
       gram_entries<TIn, MFMA>(s, 0, N, 0, N, H, dk, b, h, gdn, q, k);
       __syncthreads();
-      TV_LOAD_QK(true)
-      TV_LOAD_V(0, true)
+      // tile T holds the nodes at depth-order positions 32 T .. 32 T + 31:
+      // the lanes of a wave finish nodes of one depth, so their loops over
+      // the path entries end together
+      const int pj = 32 * wave + (tid & 31);
+      const int myn = pj < N ? s.ord[pj] : -1;
+      TV_LOAD_QK(myn, true)
+      TV_LOAD_V(myn, 0, true)
       if (gdn) tree_inverse(s, N);
       for (int cb = 0;;) {
         const int c0 = cb * vb;
         uint2 gq[4];
-        if (wave < ntiles) contract_keep(s, t0, wave, N, gdn, gq);
+        contract_keep(s, t0, myn, gdn, gq);
         const bool more = cb + 1 < nvb;
         TV_LOAD_S(c0 + vb, more)
-        TV_LOAD_V(c0 + vb, more)
+        TV_LOAD_V(myn, c0 + vb, more)
         __syncthreads();  // R rows in LDS
-        gather_owner(s, gq, wave, N, H, b, h, bh, c0, o, U);
+        gather_owner(s, gq, myn, N, H, b, h, bh, c0, o, U);
         if (more) reinterpret_cast<float4*>(s.Sst)[tid] = snext;  // the block's products are done
         __syncthreads();
         if (!more) break;
@@ -780,6 +789,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
       return;
     }
   }
+  const int idn = wave < ntiles ? identity_node(wave, N) : -1;  // tile rows: identity mapping
   if (resident) {
     // the first block's node tiles load during the inverse (not before: every
     // workgroup would fetch them at once and the tree build would wait)
@@ -787,12 +797,12 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     __syncthreads();
     gram_entries<TIn, MFMA>(s, 0, N, 0, N, H, dk, b, h, gdn, q, k);
     __syncthreads();
-    TV_LOAD_QK(true)
-    TV_LOAD_V(0, true)
+    TV_LOAD_QK(idn, true)
+    TV_LOAD_V(idn, 0, true)
     if (gdn) tree_inverse(s, N);
   } else {
-    TV_LOAD_QK(true)
-    TV_LOAD_V(0, true)
+    TV_LOAD_QK(idn, true)
+    TV_LOAD_V(idn, 0, true)
   }
   TV_CONTRACT(0)
   for (int cb = 0;;) {
@@ -815,7 +825,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     }
     const bool more = cb + 1 < nvb;
     TV_LOAD_S(c0 + vb, more)
-    TV_LOAD_QK(more)
+    TV_LOAD_QK(idn, more)
     if (resident) {
       gather_outputs(s, vb, N, H, dv, b, h, bh, c0, o, U);
     } else {
@@ -825,7 +835,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     if constexpr (MFMA) {
       if (more) reinterpret_cast<float4*>(s.Sst)[tid] = snext;  // the block's products are done
     }
-    TV_LOAD_V(c0 + vb, more)
+    TV_LOAD_V(idn, c0 + vb, more)
     __syncthreads();
     if (!more) break;
     ++cb;
