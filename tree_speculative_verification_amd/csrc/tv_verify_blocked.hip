@@ -13,34 +13,31 @@
 // over the path nodes after j, gamma_n the product over all of anc*(n).  In
 // scalar-decay mode u_n = v_n and only the second line is left.
 //
-// The solve is blocked so that any tree fits on chip.  The tree's path
-// entries (node n, ancestor j) are laid out node after node with nodes sorted
-// by depth, and processed in chunks of as many entries as LDS holds: a chunk's
-// entries get their Gram values and decays, then the chunk's nodes are solved
-// one depth level at a time (a node's ancestors all sit in earlier levels, so
-// they are final by then), then their outputs are gathered.  Only the chunk's
-// entries and the workgroup's columns of U live in LDS, so trees of any depth
-// go through the same code; a wide tree is a few chunks and one level step
-// per depth.
-//
-// One workgroup of 1024 threads per (sequence b, head h):
+// The tree's path entries (node n, ancestor j) are laid out node after node
+// with nodes sorted by depth.  One workgroup of 1024 threads handles one
+// (sequence b, head h) and loops over the value columns in blocks of up to 32:
 //   1. tree index: pointer jumping gives each node's path length and gamma;
-//      nodes are then sorted by depth (counting sort) and given entry offsets;
-// then, for each block of up to 32 value columns:
-//   2. R and gamma QS for every node into LDS: on matrix cores for bf16 with
-//      d_k = d_v = 128 (32x32x16 bf16, S split into hi + lo words; the S block
-//      and the first node tile are loaded before step 1, so their HBM latency
-//      hides under the tree build), else fp32 FMA;
-//   3. per chunk: path walk (entry nodes and decays), Gram dot products by
-//      one 8-lane group per node, four of its entries in flight at a time
-//      (the ancestor-masked Gram/decay builder), level solve, outputs (U and
-//      o stored to HBM once).  When the whole tree's entries fit in LDS (up
-//      to 4608 with bf16 inputs, 1400 with fp32) the walk and the Gram
-//      values are computed for the first column block only and reused.
+//      nodes are sorted by depth (counting sort) and given entry offsets;
+//   2. path walk (entry nodes and decays) and Gram values, one 8-lane group
+//      per node, four of its entries in flight (the ancestor-masked
+//      Gram/decay builder);
+//   3. per column block: R and gamma QS (on matrix cores for bf16 with
+//      d_k = d_v = 128, 32x32x16 bf16 with S split into hi + lo words; fp32
+//      FMA otherwise), then the solve and the outputs, U and o stored once.
 //
-// One workgroup fills most of a CU's LDS (R/U and gamma QS for 512 nodes x 32
-// columns are 96 KB with bf16 gamma QS), so a CU runs one at a time and
-// latency is hidden inside the workgroup: sixteen waves, loads issued ahead of
+// Resident trees (their entries fit in LDS: up to 3040 with bf16 inputs, 1400
+// with fp32) are walked and given Gram values once.  The solve is then a
+// product with the inverse of I + A: it is nonzero only on root paths, like A,
+// so its rows and the output weights are formed once per entry, and each
+// column block is one gather over R rows.  For bf16 at d = 128 the q and k
+// tiles also stay in registers for all column blocks and gamma QS stays in the
+// accumulator lanes.  Deeper trees go in chunks of entries, walked again for
+// every column block and solved one depth level at a time (a node's ancestors
+// sit in earlier levels, so they are final by then); any depth goes through.
+//
+// One workgroup fills most of a CU's LDS (R for 512 nodes x 32 columns, gamma
+// QS, the S block and the entries), so a CU runs one at a time and latency is
+// hidden inside the workgroup: sixteen waves, loads issued a phase ahead of
 // use.
 #include "tv_device.h"
 #include "tv_launch.h"
@@ -644,8 +641,9 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
 
   // matrix-core path: a column block's S block (128 x 32 fp32, 16 KB, one
   // float4 per thread) and the wave's node tile are loaded into registers one
-  // phase ahead of their use; those of the first block are in flight during
-  // the tree build
+  // phase ahead of their use.  The first block's S part is in flight during
+  // the tree build; its tiles load after the Gram values (before the tree
+  // build every workgroup would fetch them at once and the build would wait).
   static_assert(kBT * 4 == kBD * kBVB, "one float4 of the S block per thread");
   static_assert(kMaxTree / 32 <= kBT / 64, "a node tile per wave");
   TileIn t0;
