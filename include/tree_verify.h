@@ -81,7 +81,9 @@ extern "C" {
 #define TV_OK 0
 #define TV_ERR_NULL (-1)     /* a required pointer is NULL */
 #define TV_ERR_DIMS (-2)     /* B, H or N <= 0, N > TV_MAX_NODES (128 for the snapshot
-                                baseline), or a size overflows */
+                                baseline), or a size overflows (including one
+                                sequence's N H max(d_k, d_v) 4-byte elements
+                                past 2^32 bytes) */
 #define TV_ERR_HEAD_DIM (-3) /* d_k or d_v not in {16, 32, 64, 128} */
 #define TV_ERR_MODE (-4)     /* bad dtype or mode, or beta == NULL in GDN mode */
 #define TV_ERR_ALIAS (-5)    /* an output overlaps an input it may not overlap */

@@ -85,6 +85,14 @@ def test_verify_bad_dims(lib, B, H, N):
     assert _verify(lib, B=B, H=H, N=N) == TV_ERR_DIMS
 
 
+def test_verify_sequence_past_32bit_offsets(lib):
+    """One sequence's N H d rows must stay addressable with 32-bit byte
+    offsets: 512 nodes x 16384 heads x 128 x 4 bytes is just past 2^32."""
+    assert _verify(lib, B=1, H=1 << 14, N=512, dk=128, dv=128, dtype=1) == TV_ERR_DIMS
+    assert lib.tree_commit(1, 1 << 14, 512, 128, 128, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           None, None, None) == TV_ERR_DIMS
+
+
 @pytest.mark.parametrize("dk,dv", [(8, 16), (16, 48), (256, 128), (0, 16)])
 def test_verify_bad_head_dims(lib, dk, dv):
     assert _verify(lib, dk=dk, dv=dv) == TV_ERR_HEAD_DIM

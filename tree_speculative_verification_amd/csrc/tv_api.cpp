@@ -14,8 +14,11 @@ bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 // 64-bit addressing.
 bool sizes_ok(long long B, long long H, long long N, long long dk, long long dv) {
   const long long big = 1LL << 40;
-  return B <= big / H && B * H <= big / N && B * H * N <= big / (dk > dv ? dk : dv) &&
-         B * H <= big / (dk * dv);
+  // one sequence's q, k or v rows (N H d elements of at most 4 bytes) stay
+  // addressable with 32-bit byte offsets, as the kernels address them
+  const long long d = dk > dv ? dk : dv;
+  return B <= big / H && B * H <= big / N && B * H * N <= big / d &&
+         B * H <= big / (dk * dv) && N * H * d * 4 <= 0xffffffffLL;
 }
 
 // The snapshot buffer (B H N d_k d_v floats) stays below 2^46 bytes.
