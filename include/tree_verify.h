@@ -73,9 +73,11 @@ extern "C" {
 #define TV_ALGO_LEVEL 1   /* level-scheduled forward substitution, fp32 FMA, any d; N <= 128 */
 #define TV_ALGO_MFMA 2    /* bf16 matrix cores + per-node path solve; bf16, d_k = d_v = 128,
                              N <= 128 */
-#define TV_ALGO_BLOCKED 3 /* blocked solve over depth-sorted chunks of path entries: any tree
-                             up to TV_MAX_NODES, any depth, any d (matrix-core contraction for
-                             bf16 at d_k = d_v = 128) */
+#define TV_ALGO_BLOCKED 3 /* one workgroup per (sequence, head): any tree up to TV_MAX_NODES,
+                             any depth, any d (matrix-core contraction for bf16 at
+                             d_k = d_v = 128).  Trees whose path entries fit on chip are solved
+                             through the inverse of I + A (nonzero only on root paths), others
+                             in depth-sorted chunks of entries */
 
 /* host return codes */
 #define TV_OK 0
