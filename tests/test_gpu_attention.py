@@ -146,3 +146,20 @@ def test_repeatable_bit_for_bit():
     o1, s1 = _run(bt)
     o2, s2 = _run(bt)
     assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+def test_one_round_pairing_every_output():
+    """A grid of exactly 512 workgroups (64 sequences x 8 key/value heads x 1
+    query block) takes the ordering that pairs long and short prefixes on a
+    CU: every output checked, with prefix lengths that tie, reach 0 and
+    reach P_max."""
+    rng = np.random.default_rng(31)
+    B, N = 64, 16
+    par = np.stack([_rand_tree(rng, N) for _ in range(B)])
+    plen = rng.integers(0, 97, size=B)
+    plen[:6] = [0, 96, 96, 40, 40, 40]
+    bt = synth.make_attention_inputs(seed=31, B=B, N=N, Hq=8, Hkv=8, P_max=96, parents=par,
+                                     prefix_len=plen)
+    o, st = _run(bt)
+    assert not st.any()
+    _check(bt, o)

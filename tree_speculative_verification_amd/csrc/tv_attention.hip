@@ -38,6 +38,7 @@ constexpr int kAKeys = 32;        // keys per tile
 constexpr int kVS = kAD + 8;       // bf16 row stride of the V tile (rows 4 apart on other banks)
 constexpr int kAMaskNodes = kARows + 1;        // nodes a row block can touch
 constexpr int kAWords = kMaxTree / 32;         // ancestor words per node
+constexpr int kBalSeqs = 64;                   // sequences the one-round pairing ranks in LDS
 
 typedef __bf16 abf16x8 __attribute__((ext_vector_type(8)));
 typedef short atr4 __attribute__((ext_vector_type(4)));
@@ -75,7 +76,35 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lm = lane & 31, hi = lane >> 5;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  // A workgroup's work follows its sequence's prefix length.  A grid of 512
+  // workgroups is one round at two per CU on the 256 CUs, and the round lasts
+  // as long as its busiest CU.  The dispatcher fills every CU's first slot
+  // before any second one (workgroup k goes to XCD k % 8, its slot-0 and
+  // slot-1 workgroups are k and k + 256), so the items are ranked by prefix
+  // length and the heaviest are paired with the lightest on each CU.
+  // Consecutive ranks stay on one XCD, so the query blocks of a head still
+  // share its key/value tiles through that XCD's L2.  Other grids keep the
+  // plain order.
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  {
+    const int per_b = Hkv * nqb;
+    const int Bn = gridDim.x / per_b;
+    if (gridDim.x == 2 * 256 && Bn <= kBalSeqs) {
+      __shared__ int sP[kBalSeqs];
+      __shared__ int sel;
+      if (tid < Bn) sP[tid] = min(max(prefix_len[tid], 0), P_max);
+      __syncthreads();
+      const int k = blockIdx.x, x = k % 8, j = k / 8;
+      const int m = j < 32 ? x * 32 + j : 511 - (x * 32 + (j - 32));  // rank of the item
+      if (tid < Bn) {  // the sequence of rank m / per_b (longest prefix first, then by index)
+        int c = 0;
+        for (int t = 0; t < Bn; ++t) c += (sP[t] > sP[tid]) || (sP[t] == sP[tid] && t < tid);
+        if (c == m / per_b) sel = tid;
+      }
+      __syncthreads();
+      bid = sel * per_b + m % per_b;
+    }
+  }
   const int qb = bid % nqb;
   const int bkv = bid / nqb;
   const int kvh = bkv % Hkv;
