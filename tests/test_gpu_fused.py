@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle_pool
 from parity import TOL, max_rel
 from tree_speculative_verification_amd import synth
 
@@ -112,8 +113,59 @@ def test_fused_wide_tree_full_batch_sampled():
     _check(prev, cur, g, bs=[0, 15], hs=[5, 63])
 
 
+def test_fused_full_size_every_state():
+    """The 64-node workload at full size (B=32, H=32), the launch the benchmark times:
+    every (sequence, head) against the oracle's commit of the previous tree followed
+    by its verification of the new one."""
+    prev, cur = _pair(4)
+    g = _pipeline(prev, cur)
+    assert not g["st"].any() and not g["cst"].any()
+    ref = oracle_pool.commit_then_verify(prev, cur, [(b, list(range(cur.H))) for b in range(cur.B)])
+    path, _ = oracle.accepted_paths(prev.parents, prev.accepted)
+    np.testing.assert_array_equal(g["path"], path)
+    tol = TOL[cur.dtype]
+    errs = dict(S=max_rel(g["S"], ref["S"], 0, 1), U=max_rel(g["U"], ref["U"], 0, 1),
+                o=max_rel(g["o"], ref["o"], 0, 2))
+    assert errs["S"] <= tol["S"] and errs["U"] <= tol["U"] and errs["o"] <= tol["o"], errs
+
+
+def test_fused_wide_tree_every_sequence():
+    """128-node trees, all 128 sequences of the workload (8 heads): every residue of
+    the launch's block index."""
+    prev, cur = _pair(5, B=128, H=8)
+    g = _pipeline(prev, cur)
+    assert not g["st"].any() and not g["cst"].any()
+    ref = oracle_pool.commit_then_verify(prev, cur, [(b, list(range(cur.H))) for b in range(cur.B)])
+    path, _ = oracle.accepted_paths(prev.parents, prev.accepted)
+    np.testing.assert_array_equal(g["path"], path)
+    tol = TOL[cur.dtype]
+    errs = dict(S=max_rel(g["S"], ref["S"], 0, 1), U=max_rel(g["U"], ref["U"], 0, 1),
+                o=max_rel(g["o"], ref["o"], 0, 2))
+    assert errs["S"] <= tol["S"] and errs["U"] <= tol["U"] and errs["o"] <= tol["o"], errs
+
+
 def test_fused_inplace():
     prev, cur = _pair(4, 2, 4)
+    g = _pipeline(prev, cur, inplace=True)
+    _check(prev, cur, g)
+
+
+@pytest.mark.parametrize("Np,N,deep", [(8, 20, False), (64, 32, False), (40, 64, False),
+                                        (64, 100, False), (128, 128, False), (30, 40, True),
+                                        (64, 128, True)])
+def test_fused_inplace_every_shape(Np, N, deep):
+    """S_out == S_in for each kernel shape the new tree selects: 32-node tiles,
+    64-node, 128-node (several node tiles sharing one state block), and a new tree
+    with a path longer than 16 (the commit runs first, then the level solve reads
+    the committed state back)."""
+    rng = np.random.default_rng(Np * 7 + N + deep)
+    par_p = np.stack([_random(rng, Np) for _ in range(3)])
+    if deep:
+        par_c = np.stack([_chain(N), _random(rng, N, depth=N, fan=2), _random(rng, N)])
+    else:
+        par_c = np.stack([_random(rng, N) for _ in range(3)])
+    acc = np.array([Np - 1, Np // 2, 0], np.int32)
+    prev, cur = _custom_pair(par_p, acc, par_c, H=3, seed=Np + N)
     g = _pipeline(prev, cur, inplace=True)
     _check(prev, cur, g)
 

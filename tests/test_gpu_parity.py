@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle_pool
 from parity import TOL, compare, max_rel, run_gpu, run_oracle
 from tree_speculative_verification_amd import synth
 
@@ -100,6 +101,44 @@ def test_full_size_sampled(cfg, algo):
     # integer outputs for every sequence, checked against the oracle's walk
     path_ref, st_ref = oracle.accepted_paths(bt.parents, bt.accepted)
     assert np.array_equal(gpu["path"], path_ref)
+    assert not gpu["status_v"].any() and not gpu["status_c"].any()
+
+
+def test_full_size_every_state_64_node():
+    """The 64-node workload at full size (B=32, H=32), as the benchmark launches it:
+    every (sequence, head) state of the launch against the oracle (verify + commit)."""
+    bt = cfg_batch(4)
+    gpu = run_gpu(bt)
+    ref = oracle_pool.verify_commit(bt, [(b, list(range(bt.H))) for b in range(bt.B)])
+    assert not gpu["status_v"].any() and not gpu["status_c"].any()
+    path_ref, _ = oracle.accepted_paths(bt.parents, bt.accepted)
+    assert np.array_equal(gpu["path"], path_ref)
+    _check(bt, gpu, ref)
+
+
+def _diag(gpu, ref, pairs):
+    """The listed (b, h) slices of both sides as [P, ..., 1, ...] arrays for compare()."""
+    g = dict(o=np.stack([gpu["o"][b, :, h] for b, h in pairs])[:, :, None],
+             U=np.stack([gpu["U"][b, h] for b, h in pairs])[:, None],
+             S=np.stack([gpu["S"][b, h] for b, h in pairs])[:, None])
+    r = dict(o=np.stack([ref["o"][b, :, h] for b, h in pairs])[:, :, None],
+             U=np.stack([ref["U"][b, h] for b, h in pairs])[:, None],
+             S=np.stack([ref["S"][b, h] for b, h in pairs])[:, None])
+    return g, r
+
+
+def test_full_size_every_sequence_128_node():
+    """The 128-node workload at full size (B=128, H=64): every sequence, two heads
+    each (h = b mod 64 and (7b + 3) mod 64), so every head and every residue of the
+    launch's block index is checked against the oracle."""
+    bt = cfg_batch(5)
+    gpu = run_gpu(bt)
+    heads = [sorted({b % bt.H, (7 * b + 3) % bt.H}) for b in range(bt.B)]
+    ref = oracle_pool.verify_commit(bt, list(zip(range(bt.B), heads)))
+    pairs = [(b, h) for b in range(bt.B) for h in heads[b]]
+    g, r = _diag(gpu, ref, pairs)
+    ok, errs = compare(g, r, bt.dtype)
+    assert ok, errs
     assert not gpu["status_v"].any() and not gpu["status_c"].any()
 
 
