@@ -15,11 +15,14 @@ Cold caches without flush kernels: R copies of the input set (>= 1 GB in all,
 far above the 256 MB Infinity Cache and the L2s) are used in turn, and a
 step's commit takes the batch verified two steps earlier, so every kernel
 streams its operands from HBM, as it would with the rest of a model forward
-between verify and commit.  W warm-up steps, then K timed steps between one
-pair of HIP events on the launch stream (bracketed by device
-synchronizations).  ms_per_step is that time / K; value = B*N / ms_per_step
-of the fused pipeline.  Per-kernel durations for the roofline come from K
-back-to-back launches of each kernel over the same ring.
+between verify and commit.  Warm-up: at least W steps and at least 250 ms of
+GPU time (the clocks ramp over the first tens of milliseconds, so a count
+alone makes short runs read slow), then, before each timed loop, 30 ms of
+that loop's own body.  K timed steps run between one pair of HIP events on
+the launch stream (bracketed by device synchronizations).  ms_per_step is
+that time / K; value = B*N / ms_per_step of the fused pipeline.  Per-kernel
+durations for the roofline come from K back-to-back launches of each kernel
+over the same ring.
 
 Prints ONE JSON line.  Options: --steps K --warmup W --gpus 1 (only 1 is
 supported: the path runs on one GPU) --workload {3,4,5,6} --no-cpu-baseline.
@@ -44,6 +47,12 @@ import numpy as np  # noqa: E402
 from tree_speculative_verification_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+# worker processes of the CPU oracle baseline: the host share of one GPU
+CPU_WORKER_CAP = 16
+# warm-up: at least this much GPU time before the first timed launch (clocks ramp
+# over the first tens of milliseconds), and this much per timed body before its loop
+WARM_MS = 250.0
+WARM_BODY_MS = 30.0
 METRIC = "verified tree nodes/s per GDN layer (1 GPU) + % of HBM roofline"
 _CSRC = "tree_speculative_verification_amd/csrc/"
 KERNEL_SOURCES = {
@@ -136,7 +145,8 @@ def cpu_baseline(bt, max_seqs, reps):
         os.environ[var] = "1"
     _CPU_BATCH = bt
     seqs = list(range(min(bt.B, max_seqs))) * reps
-    cores = min(len(os.sched_getaffinity(0)), 16, len(seqs))
+    avail = len(os.sched_getaffinity(0))
+    cores = min(avail, CPU_WORKER_CAP, len(seqs))
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(cores) as pool:
@@ -151,11 +161,30 @@ def cpu_baseline(bt, max_seqs, reps):
                     break
     except OSError:
         pass
-    return {"value": len(seqs) * bt.N / wall, "unit": "nodes/s", "cores": cores, "kind": "oracle",
+    return {"value": len(seqs) * bt.N / wall, "unit": "nodes/s", "cores": cores,
+            "cores_available": avail, "kind": "oracle",
             "sample": f"{len(seqs) // reps} of {bt.B} sequences x all {bt.H} heads of the same "
                       f"workload, {reps} passes (fp64 token-by-token path walk, verify + commit), "
-                      f"wall {wall:.2f} s on {cores} worker processes, 1 BLAS thread each; "
+                      f"wall {wall:.2f} s on {cores} worker processes ({avail} cores available "
+                      f"to this process, at most {CPU_WORKER_CAP} used), 1 BLAS thread each; "
                       f"{cpu_model}"}
+
+
+def warm_up(body, min_calls, min_ms):
+    """Runs body(i) at least min_calls times and until min_ms of wall time has passed
+    with the GPU busy (synchronizing every few calls); returns (calls, ms)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(8):
+            body(i)
+            i += 1
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        if i >= min_calls and ms >= min_ms:
+            return i, ms
 
 
 # ------------------------------------------------------ tree attention leg
@@ -204,14 +233,15 @@ def attention_cpu_baseline(bt, pairs):
     _ATTN_BATCH = bt
     B, N, Hq, _ = bt.q.shape
     work = [(b, h) for b in range(B) for h in range(Hq)][:pairs]
-    cores = min(len(os.sched_getaffinity(0)), 16, len(work))
+    avail = len(os.sched_getaffinity(0))
+    cores = min(avail, CPU_WORKER_CAP, len(work))
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(cores) as pool:
         list(pool.imap_unordered(_oracle_attn_seq, work))
     wall = time.perf_counter() - t0
     # one sequence's N nodes need all Hq heads: nodes/s = pairs * N / Hq / wall
     return {"value": len(work) * N / Hq / wall, "unit": "nodes/s", "cores": cores,
-            "kind": "oracle",
+            "cores_available": avail, "kind": "oracle",
             "sample": f"{len(work)} (sequence, query head) pairs of the workload, all {N} nodes "
                       f"each (fp64 masked softmax per node), scaled to whole nodes (all {Hq} "
                       f"heads); wall {wall:.2f} s on {cores} worker processes"}
@@ -243,9 +273,7 @@ def attention_main(a):
                       t["v_tree"], t["parents"], t["scale"], o=t["o"], status=t["st"],
                       stream=stream)
 
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_calls, warm_ms = warm_up(step, a.warmup, WARM_MS)
     if any(t["st"].any().item() for t in sets):
         raise RuntimeError("device status reported bad input rows")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -262,6 +290,7 @@ def attention_main(a):
     out = {
         "metric": ATTN_METRIC, "value": round(B * N / (ms * 1e-3), 1), "unit": "nodes/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "warmup_done": {"calls": warm_calls, "ms": round(warm_ms, 1)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": synth.ATTN_NAME, "B": B, "N": N, "Hq": Hq,
@@ -436,18 +465,24 @@ def main(argv=None):
         verify(i)
         commit(i - 2)
 
-    for i in range(a.warmup):
+    def both(i):
         step2(i)
         fused(i)
-    torch.cuda.synchronize()
+
+    warm_calls, warm_ms = warm_up(both, a.warmup, WARM_MS)
     for t in sets:
         if t["st_v"].any().item() or t["st_c"].any().item():
             raise RuntimeError("device status reported bad input rows")
 
-    ms_step, wall_ms = timed(fused, a.steps)
-    ms_two, _ = timed(step2, a.steps)
-    tv_ms, _ = timed(verify, a.steps)
-    tc_ms, _ = timed(commit, a.steps)
+    def timed_warm(body, k):
+        """K timed launches of body, after WARM_BODY_MS of the same body."""
+        warm_up(body, 4, WARM_BODY_MS)
+        return timed(body, k)
+
+    ms_step, wall_ms = timed_warm(fused, a.steps)
+    ms_two, _ = timed_warm(step2, a.steps)
+    tv_ms, _ = timed_warm(verify, a.steps)
+    tc_ms, _ = timed_warm(commit, a.steps)
 
     base = None
     snap_bytes = B * H * N * dk * dv * 4
@@ -479,6 +514,8 @@ def main(argv=None):
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
+        "warmup_done": {"calls": warm_calls, "ms": round(warm_ms, 1),
+                        "per_body_ms": WARM_BODY_MS},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[a.workload], "B": B, "H": H, "N": N,

@@ -101,6 +101,12 @@ extern "C" {
 /*
  * tree_verify -- outputs of all N draft nodes of B sequences x H heads in one
  * launch, plus the pseudo-value matrix U that tree_commit needs.
+ * Defined by: TreeWY abstract (every draft node's output from one
+ * tree-structured WY triangular solve; a small pseudo-value matrix kept in
+ * place of per-node states) and Twig abstract (all draft nodes verified in
+ * parallel by one kernel); for scalar decay, the Bole auto-summary's core
+ * formulas and worked example (node state = decayed root state plus the
+ * decayed k v^T terms of its root path).
  *
  *   q, k      [B, N, H, dk]  dtype, contiguous
  *   v         [B, N, H, dv]  dtype, contiguous
@@ -119,7 +125,8 @@ int tree_verify(int B, int H, int N, int dk, int dv, int dtype, int mode, const 
 
 /* tree_verify with an explicit solver choice (TV_ALGO_*); same outputs within
  * floating-point rounding.  TV_ERR_ALGO when the choice does not apply to the
- * arguments.  Used by tests to exercise every solver on the same inputs. */
+ * arguments.  Used by tests to exercise every solver on the same inputs.
+ * Defined by: the TreeWY abstract, as tree_verify. */
 int tree_verify_algo(int B, int H, int N, int dk, int dv, int dtype, int mode, const void* q,
                      const void* k, const void* v, const float* alpha, const float* beta,
                      const int32_t* parents, const float* S_root, void* o, float* U,
@@ -128,6 +135,11 @@ int tree_verify_algo(int B, int H, int N, int dk, int dv, int dtype, int mode, c
 /*
  * tree_commit -- state after the accepted node of each sequence, from S_root
  * and the token-level factors (k, alpha, U) of that node's root path only.
+ * Defined by: TreeWY abstract (only the one accepted state is reconstructed,
+ * on commit), Twig abstract (speculative updates kept as token-level factors,
+ * only the accepted state rebuilt) and the Bole auto-summary's reconstruction
+ * formula and its c3 worked example (the path's per-token factors applied to
+ * the old root state).
  *
  *   k         [B, N, H, dk]  dtype     (as passed to tree_verify)
  *   alpha     [B, N, H] f32
@@ -150,7 +162,10 @@ int tree_commit(int B, int H, int N, int dk, int dv, int dtype, const void* k, c
 
 /*
  * tree_index -- the tree bookkeeping both kernels do internally, exposed for
- * bit-exact testing.
+ * bit-exact testing.  Defined by: the Bole auto-summary's worked example
+ * (each draft node's state follows its own root path; branches may hang
+ * directly off the root state) and Twig abstract (the draft is a tree of
+ * candidate tokens).
  *   parents [B, N] int32
  *   depth   [B, N] int32 OUT   (parent -1 -> depth 0)
  *   anc     [B, N, (N+63)/64] uint64 OUT: bit j%64 of word j/64 set when node j
@@ -184,7 +199,9 @@ int tree_verify_snapshot(int B, int H, int N, int dk, int dv, int dtype, int mod
  * tree_commit_snapshot -- the baseline's commit: S_out[b, h] = snapshots[b, h,
  * accepted[b]] (node 0 for a bad accepted index), plus path_out and status
  * with the conventions of tree_commit.  S_out must not overlap snapshots
- * (TV_ERR_ALIAS).
+ * (TV_ERR_ALIAS).  Defined by: Twig abstract and Bole abstract (the engines
+ * compared against keep a full state per draft node and take the accepted
+ * node's snapshot).
  */
 int tree_commit_snapshot(int B, int H, int N, int dk, int dv, const float* snapshots,
                          const int32_t* parents, const int32_t* accepted, float* S_out,
@@ -263,10 +280,12 @@ int tree_attention(int B, int N, int Hq, int Hkv, int D, int P_max, int dtype, c
                    const void* k_tree, const void* v_tree, const int32_t* parents, float scale,
                    void* o, int32_t* status, void* stream);
 
-/* Text for a return code (negative) or a status code (0..3). Never NULL. */
+/* Text for a return code (negative) or a status code (0..3). Never NULL.
+ * Library bookkeeping: defined by this header, no passage of the pages. */
 const char* tv_status_string(int code);
 
-/* ABI version: major * 100 + minor. */
+/* ABI version: major * 100 + minor.
+ * Library bookkeeping: defined by this header, no passage of the pages. */
 int tv_version(void);
 
 #ifdef __cplusplus

@@ -47,6 +47,27 @@ def test_header_declares_expected():
                                            "tree_attention", "tv_status_string", "tv_version"])
 
 
+def _doc_blocks():
+    """Each declared function with the comment block right above its declaration."""
+    text = open(HEADER).read()
+    out = {}
+    for m in re.finditer(r"/\*((?:(?!\*/).)*)\*/\s*((?:const\s+)?\w+\s*\*?\s*(\w+)\s*\()", text, flags=re.S):
+        out[m.group(3)] = m.group(1)
+    return out
+
+
+def test_every_declaration_cites_its_passage():
+    """Every entry point's comment names the page passage that defines it (the
+    pages by title and section), or says that it is library bookkeeping."""
+    blocks = _doc_blocks()
+    pages = re.compile(r"(TreeWY|Twig|Bole)[^.]*(abstract|auto-summary|worked example|core formula|"
+                       r"reconstruction formula)", flags=re.S | re.I)
+    for name in declared_functions():
+        assert name in blocks, f"{name} has no comment block"
+        doc = blocks[name]
+        assert pages.search(doc) or "Library bookkeeping" in doc or "cannot allocate" in doc, name
+
+
 def test_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -214,3 +235,29 @@ def test_attention_checks(lib):
     assert call(Pm=-1) == TV_ERR_DIMS
     assert call(D=64) == TV_ERR_HEAD_DIM
     assert call(dtype=0) == TV_ERR_MODE
+
+
+def test_host_checks_under_address_and_ub_sanitizers(tmp_path):
+    """tv_api.cpp built for the CPU alone (g++, no device code) with AddressSanitizer
+    and UBSan, linked against launchers that only count calls: every entry point
+    with good and bad arguments; bad ones must return their code and launch nothing."""
+    import shutil
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("needs g++ and the ROCm headers")
+    here = os.path.join(ROOT, "tests", "host_sanitize")
+    exe = str(tmp_path / "abi_asan")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I" + os.path.join(ROOT, "include"),
+           "-I" + os.path.join(ROOT, "tree_speculative_verification_amd", "csrc"),
+           os.path.join(ROOT, "tree_speculative_verification_amd", "csrc", "tv_api.cpp"),
+           os.path.join(here, "stub_launchers.cpp"), os.path.join(here, "abi_driver.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    # another preloaded library may come before the ASan runtime: allow that order
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+    assert r.stdout.startswith("ok:"), r.stdout

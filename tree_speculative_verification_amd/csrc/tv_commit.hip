@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads, NMAX > kMaxNodes ? 4 : 1) void commit_ker
   __shared__ __align__(16) float ksh[CH][RT];
 
   const int tid = threadIdx.x;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bid = blockIdx.x;  // dispatch order: the workgroups share no large inputs
   const int tile = bid % ntiles;
   const int bh = bid / ntiles;
   const int h = bh % H;

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(kThreads) void verify_level_kernel(
   __shared__ TreeLds t;
   __shared__ LevelLds s;
   const int nvb = dv / cb;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bid = xcd_group(blockIdx.x, gridDim.x, nvb);
   const int vb = bid % nvb;
   const int bh = bid / nvb;
   const int h = bh % H;

@@ -276,7 +276,7 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   const int lm = lane & 31;
   const int hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: wave-uniform branches
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bid = xcd_group(blockIdx.x, gridDim.x, NVB);
   const int vb = bid % NVB;
   const int bh = bid / NVB;
   const int h = bh % H;
