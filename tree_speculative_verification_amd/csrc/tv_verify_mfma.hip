@@ -260,13 +260,15 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   // fused commit: the previous tree's accepted path (first 16 nodes)
   struct PrevPathLds {
     float pd[16];   // D(e_t -> a), 0 past the end
+    int e[16];      // e_t: node at distance t (node 0 past the end)
     float gam;      // gamma_a
     float cn;       // D at distance 16
     int next;       // node at distance 16, or -1
   };
   __shared__ __align__(16) PrevPathLds spath;
   // fused commit: k rows [16][128] bf16 and u columns [16][VB] f32 of those
-  // nodes, staged by wave 1; in XW (unused until the path solve) where it fits
+  // nodes, fetched by every wave under the Gram; in XW (unused until the path
+  // solve) where it fits
   constexpr int kStageBytes = 16 * kD * 2 + 16 * VB * 4;
   constexpr bool kStageInXW = (int)sizeof(float2) * kMaxL * NP >= kStageBytes;
   __shared__ __align__(16) unsigned char pstage[(FUSED && !kStageInXW) ? kStageBytes : 16];
@@ -449,30 +451,18 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
     const int next = node;
     const float cn = c;
     for (int n2 = node; n2 >= 0; n2 = node_lane_i(ppar, n2)) c = uniform_f(c * node_lane_f(pal, n2));
-    if (lane < 16) spath.pd[lane] = my_d;
+    if (lane < 16) {
+      spath.pd[lane] = my_d;
+      spath.e[lane] = my_e;
+    }
     if (lane == 0) {
       spath.gam = c;
       spath.cn = cn;
       spath.next = next;
     }
-    // Stage their k rows ([j][128] bf16, 4 rows an instruction) and u columns
-    // ([j][VB] f32) with LDS DMA, 16 bytes a lane; every source node first
-    // (cross-lane reads), then every copy, so no copy waits on another.
-    constexpr int CPJ = VB / 4;  // 16-byte chunks of a u row
-    int ek[4], eu[VB / 16];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ek[r] = __shfl(my_e, 4 * r + (lane >> 4));
-#pragma unroll
-    for (int r = 0; r < VB / 16; ++r) eu[r] = __shfl(my_e, (64 / CPJ) * r + lane / CPJ);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      __builtin_amdgcn_global_load_lds(pc.k + ((size_t)(b * pc.N + ek[r]) * H + h) * kD + (lane & 15) * 8,
-                                       Pst + r * 1024, 16, 0, 0);
-#pragma unroll
-    for (int r = 0; r < VB / 16; ++r)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const uint16_t*>(pc.U + ((size_t)bh * pc.N + eu[r]) * kD + cbase + (lane % CPJ) * 4),
-          Pst + 16 * kD * 2 + r * 1024, 16, 0, 0);
+    // The path's k rows and u columns are fetched by every wave after the
+    // barrier (they are first needed by the update after the Gram), so this
+    // wave's walk is not followed by a second round trip before the barrier.
     // status and root-first path of the previous step (one wave per sequence)
     if (h == 0 && vb == 0) {
       if (pc.status && lane == 0) pc.status[b] = pbad ? 1 : (bad_acc ? 2 : 0);
@@ -497,7 +487,6 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);  // the staged rows have landed
   } else {
     const int slot = lane & 15;
     // 4-row blocks: K, then Q (waves 2 and 3 only when wave 1 stages the commit)
@@ -697,6 +686,29 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
     return;
   }
 
+  // Fused commit: the previous path's k rows ([16][128] bf16) and u columns
+  // ([16][VB] f32) in 16-byte chunks spread over the workgroup's threads, loaded
+  // into registers before the S stream (loads retire in order, so waiting for
+  // them does not wait for S) and written to the staging area after the Gram.
+  constexpr int kKChunks = 16 * kD * 2 / 16;           // 256
+  constexpr int kUChunks = 16 * VB * 4 / 16;           // 4 VB
+  constexpr int kPerThK = (kKChunks + NTH - 1) / NTH;
+  constexpr int kPerThU = (kUChunks + NTH - 1) / NTH;
+  uint4 prow_k[FUSED ? kPerThK : 1], prow_u[FUSED ? kPerThU : 1];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int r = 0; r < kPerThK; ++r) {
+      const int c = min(tid + NTH * r, kKChunks - 1);  // clamped; only in-range chunks are stored
+      const int e = spath.e[c >> 4];
+      prow_k[r] = *reinterpret_cast<const uint4*>(pc.k + ((size_t)(b * pc.N + e) * H + h) * kD + (c & 15) * 8);
+    }
+#pragma unroll
+    for (int r = 0; r < kPerThU; ++r) {
+      const int c = min(tid + NTH * r, kUChunks - 1);
+      const int e = spath.e[c / (VB / 4)];
+      prow_u[r] = *reinterpret_cast<const uint4*>(pc.U + ((size_t)bh * pc.N + e) * kD + cbase + (c % (VB / 4)) * 4);
+    }
+  }
   // S and V (at the positions the outputs land on) arrive during the Gram and
   // the path solve
   load_S();
@@ -766,7 +778,15 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
       }
     }
   }
-  __syncthreads();  // path Gram entries visible
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int r = 0; r < kPerThK; ++r)
+      if (tid + NTH * r < kKChunks) reinterpret_cast<uint4*>(Pst)[tid + NTH * r] = prow_k[r];
+#pragma unroll
+    for (int r = 0; r < kPerThU; ++r)
+      if (tid + NTH * r < kUChunks) reinterpret_cast<uint4*>(Pst + 16 * kD * 2)[tid + NTH * r] = prow_u[r];
+  }
+  __syncthreads();  // path Gram entries and the previous path's rows visible
   if constexpr (FUSED) {
     commit_prev();
     // staged rows read (the path solve writes XW); where several waves hold
