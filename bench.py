@@ -273,7 +273,7 @@ def attention_main(a):
                       t["v_tree"], t["parents"], t["scale"], o=t["o"], status=t["st"],
                       stream=stream)
 
-    warm_calls, warm_ms = warm_up(step, a.warmup, WARM_MS)
+    warm_calls, warm_ms = warm_up(step, a.warmup, a.warmup_ms)
     if any(t["st"].any().item() for t in sets):
         raise RuntimeError("device status reported bad input rows")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -374,6 +374,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup-ms", type=float, default=WARM_MS,
+                    help="least GPU time of warm-up before timing (0 for short profiled runs)")
     ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
@@ -469,14 +471,16 @@ def main(argv=None):
         step2(i)
         fused(i)
 
-    warm_calls, warm_ms = warm_up(both, a.warmup, WARM_MS)
+    warm_calls, warm_ms = warm_up(both, a.warmup, a.warmup_ms)
     for t in sets:
         if t["st_v"].any().item() or t["st_c"].any().item():
             raise RuntimeError("device status reported bad input rows")
 
+    body_ms = WARM_BODY_MS if a.warmup_ms > 0 else 0.0
+
     def timed_warm(body, k):
         """K timed launches of body, after WARM_BODY_MS of the same body."""
-        warm_up(body, 4, WARM_BODY_MS)
+        warm_up(body, 1, body_ms)
         return timed(body, k)
 
     ms_step, wall_ms = timed_warm(fused, a.steps)
@@ -515,7 +519,7 @@ def main(argv=None):
         "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
         "warmup_done": {"calls": warm_calls, "ms": round(warm_ms, 1),
-                        "per_body_ms": WARM_BODY_MS},
+                        "per_body_ms": body_ms},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES[a.workload], "B": B, "H": H, "N": N,

@@ -235,6 +235,7 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   constexpr int NW = NT * CT;                 // waves
   constexpr int NTH = 64 * NW;                // threads
   static_assert(NW == 4 || NW == 8, "one (node tile, column tile) pair per wave");
+  static_assert(NT != 2 || Lay::bytes >= 4 * 8 * 64 * 16, "room for four waves' partial products");
   constexpr int NVB = kD / VB;
   constexpr int SL = NP > 64 ? 2 : 1;         // tree nodes per lane
   constexpr int NG = NT * (NT + 1);           // lower-triangular blocks of K K^T and K Q^T
@@ -266,12 +267,6 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
     int next;       // node at distance 16, or -1
   };
   __shared__ __align__(16) PrevPathLds spath;
-  // fused commit: k rows [16][128] bf16 and u columns [16][VB] f32 of those
-  // nodes, fetched by every wave under the Gram; in XW (unused until the path
-  // solve) where it fits
-  constexpr int kStageBytes = 16 * kD * 2 + 16 * VB * 4;
-  constexpr bool kStageInXW = (int)sizeof(float2) * kMaxL * NP >= kStageBytes;
-  __shared__ __align__(16) unsigned char pstage[(FUSED && !kStageInXW) ? kStageBytes : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -306,7 +301,6 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   // there.  Wave 0 issues none of these, so nothing delays its tree build.
   uint16_t* Ksh = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Qsh = Ksh + NP * kD;
-  unsigned char* const Pst = kStageInXW ? reinterpret_cast<unsigned char*>(XW) : pstage;
   // Fused commit: the previous tree's parents and gates (nodes lane and
   // lane + 64).  Wave 1 (which stages no K/Q rows then) loads them, walks the
   // accepted path and stages its k rows and u columns while wave 0 builds the
@@ -539,6 +533,25 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   // and one 32-bit load of k at rows (2 m, 2 m + 1) feeds both tau.
   uint32_t kpd[TL / 2][8];  // k_{e_j} at rows 64 T + 2 lm (+1), j = 8 hi + i
   float upa[8];             // u_{e_j} at this lane's column
+  // The operands come straight from memory (the path's nodes are in LDS after
+  // the first barrier).  They are issued before the S stream and consumed after
+  // the path solve; the 32-node shape, whose registers are at their limit
+  // there, issues them at the update instead.
+  constexpr bool kEarlyOps = !(KS == 1 && NT == 1);
+  auto load_prev_ops = [&]() {
+    const int4 e0 = reinterpret_cast<const int4*>(spath.e)[2 * hi];
+    const int4 e1 = reinterpret_cast<const int4*>(spath.e)[2 * hi + 1];
+    const int ej[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+    const int col = cbase + ct_w * 32 + lm;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      upa[i] = pc.U[((size_t)bh * pc.N + ej[i]) * kD + col];
+#pragma unroll
+      for (int T = 0; T < TL / 2; ++T)
+        kpd[T][i] = *reinterpret_cast<const uint32_t*>(
+            pc.k + ((size_t)(b * pc.N + ej[i]) * H + h) * kD + srow0 + 64 * T + 2 * lm);
+    }
+  };
   auto prev_apply = [&](const float (&dj)[8]) {
     float x[8];
 #pragma unroll
@@ -577,16 +590,8 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
 #pragma unroll
       for (int i = 0; i < 8; ++i) sv[ks][i] *= gam;
     {
-      // first 16 path nodes from the rows wave 1 staged
-      const uint16_t* Ks = reinterpret_cast<const uint16_t*>(Pst);
-      const float* Us = reinterpret_cast<const float*>(Pst + 16 * kD * 2);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        upa[i] = Us[(8 * hi + i) * VB + ct_w * 32 + lm];
-#pragma unroll
-        for (int T = 0; T < TL / 2; ++T)
-          kpd[T][i] = *reinterpret_cast<const uint32_t*>(Ks + (8 * hi + i) * kD + srow0 + 64 * T + 2 * lm);
-      }
+      // first 16 path nodes
+      if constexpr (!kEarlyOps) load_prev_ops();
       const float4 d0 = reinterpret_cast<const float4*>(spath.pd)[2 * hi];
       const float4 d1 = reinterpret_cast<const float4*>(spath.pd)[2 * hi + 1];
       const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
@@ -686,29 +691,11 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
     return;
   }
 
-  // Fused commit: the previous path's k rows ([16][128] bf16) and u columns
-  // ([16][VB] f32) in 16-byte chunks spread over the workgroup's threads, loaded
-  // into registers before the S stream (loads retire in order, so waiting for
-  // them does not wait for S) and written to the staging area after the Gram.
-  constexpr int kKChunks = 16 * kD * 2 / 16;           // 256
-  constexpr int kUChunks = 16 * VB * 4 / 16;           // 4 VB
-  constexpr int kPerThK = (kKChunks + NTH - 1) / NTH;
-  constexpr int kPerThU = (kUChunks + NTH - 1) / NTH;
-  uint4 prow_k[FUSED ? kPerThK : 1], prow_u[FUSED ? kPerThU : 1];
-  if constexpr (FUSED) {
-#pragma unroll
-    for (int r = 0; r < kPerThK; ++r) {
-      const int c = min(tid + NTH * r, kKChunks - 1);  // clamped; only in-range chunks are stored
-      const int e = spath.e[c >> 4];
-      prow_k[r] = *reinterpret_cast<const uint4*>(pc.k + ((size_t)(b * pc.N + e) * H + h) * kD + (c & 15) * 8);
-    }
-#pragma unroll
-    for (int r = 0; r < kPerThU; ++r) {
-      const int c = min(tid + NTH * r, kUChunks - 1);
-      const int e = spath.e[c / (VB / 4)];
-      prow_u[r] = *reinterpret_cast<const uint4*>(pc.U + ((size_t)bh * pc.N + e) * kD + cbase + (c % (VB / 4)) * 4);
-    }
-  }
+  // Fused commit: this lane's operands of the update, straight from memory in
+  // the matrix-core layout (k of path node 8 hi + i at rows 64 T + 2 lm and
+  // + 1 of the wave's S rows, u of that node at the lane's column), issued
+  // before the S stream; they are consumed after the path solve.
+  if constexpr (FUSED && kEarlyOps) load_prev_ops();
   // S and V (at the positions the outputs land on) arrive during the Gram and
   // the path solve
   load_S();
@@ -778,22 +765,7 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
       }
     }
   }
-  if constexpr (FUSED) {
-#pragma unroll
-    for (int r = 0; r < kPerThK; ++r)
-      if (tid + NTH * r < kKChunks) reinterpret_cast<uint4*>(Pst)[tid + NTH * r] = prow_k[r];
-#pragma unroll
-    for (int r = 0; r < kPerThU; ++r)
-      if (tid + NTH * r < kUChunks) reinterpret_cast<uint4*>(Pst + 16 * kD * 2)[tid + NTH * r] = prow_u[r];
-  }
-  __syncthreads();  // path Gram entries and the previous path's rows visible
-  if constexpr (FUSED) {
-    commit_prev();
-    // staged rows read (the path solve writes XW); where several waves hold
-    // the same block, also every wave's S values are in before one of them
-    // stores over S_in
-    if constexpr (kStageInXW || (KS == 1 && NT > 1)) __syncthreads();
-  }
+  __syncthreads();  // path Gram entries visible
 
   // ---- 4. path solve: lane = (node my_n, chain hi) in every wave ----
   // Distance order e_0 = n, e_1 = parent(n), ...  Chain 0 gives x (u_n = sum_t
@@ -856,6 +828,13 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
                     e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24),
                     e[8] | (e[9] << 8) | (e[10] << 16) | (e[11] << 24),
                     e[12] | (e[13] << 8) | (e[14] << 16) | (e[15] << 24));
+  }
+
+  if constexpr (FUSED) {
+    commit_prev();
+    // where several waves hold the same block, every wave's S values are in
+    // before one of them stores over S_in
+    if constexpr (KS == 1 && NT > 1) __syncthreads();
   }
 
   // ---- 5. Y^T = S_block^T [K;Q]^T on matrix cores ----
@@ -933,28 +912,39 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
     }
     __syncthreads();  // K/Q staging is dead: it carries the partial products now
     // wave w hands its partial for the partner's tile to the partner (w ^ 1),
-    // as float4 groups [wave][group][lane] (consecutive lanes, no conflicts)
-    float4* xo = reinterpret_cast<float4*>(smem) + wave * (8 * 64) + lane;
+    // as float4 groups [slot][group][lane] (consecutive lanes, no conflicts);
+    // the staging area holds four waves' partials, so eight waves go in two
+    // rounds of four (pairs never straddle a round)
+    constexpr int kRounds = NW / 4;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      xo[g * 64] = make_float4(kx[4 * g], kx[4 * g + 1], kx[4 * g + 2], kx[4 * g + 3]);
-      xo[(4 + g) * 64] = make_float4(qx[4 * g], qx[4 * g + 1], qx[4 * g + 2], qx[4 * g + 3]);
-    }
-    __syncthreads();  // partials visible
-    const float4* xi = reinterpret_cast<const float4*>(smem) + (wave ^ 1) * (8 * 64) + lane;
+    for (int rnd = 0; rnd < kRounds; ++rnd) {
+      const bool mine = wave / 4 == rnd;  // uniform
+      if (mine) {
+        float4* xo = reinterpret_cast<float4*>(smem) + (wave & 3) * (8 * 64) + lane;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 pk = xi[g * 64], pq = xi[(4 + g) * 64];
-      kacc[4 * g] += pk.x;
-      kacc[4 * g + 1] += pk.y;
-      kacc[4 * g + 2] += pk.z;
-      kacc[4 * g + 3] += pk.w;
-      qacc[4 * g] += pq.x;
-      qacc[4 * g + 1] += pq.y;
-      qacc[4 * g + 2] += pq.z;
-      qacc[4 * g + 3] += pq.w;
+        for (int g = 0; g < 4; ++g) {
+          xo[g * 64] = make_float4(kx[4 * g], kx[4 * g + 1], kx[4 * g + 2], kx[4 * g + 3]);
+          xo[(4 + g) * 64] = make_float4(qx[4 * g], qx[4 * g + 1], qx[4 * g + 2], qx[4 * g + 3]);
+        }
+      }
+      __syncthreads();  // partials visible
+      if (mine) {
+        const float4* xi = reinterpret_cast<const float4*>(smem) + ((wave ^ 1) & 3) * (8 * 64) + lane;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 pk = xi[g * 64], pq = xi[(4 + g) * 64];
+          kacc[4 * g] += pk.x;
+          kacc[4 * g + 1] += pk.y;
+          kacc[4 * g + 2] += pk.z;
+          kacc[4 * g + 3] += pk.w;
+          qacc[4 * g] += pq.x;
+          qacc[4 * g + 1] += pq.y;
+          qacc[4 * g + 2] += pq.z;
+          qacc[4 * g + 3] += pq.w;
+        }
+      }
+      __syncthreads();  // partials consumed (the next round's, or R, take their place)
     }
-    __syncthreads();  // partials consumed (R takes their place)
   }
 
   // ---- 6. R = beta (V - gamma KS) into LDS rows ----
