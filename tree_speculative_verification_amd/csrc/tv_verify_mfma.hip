@@ -68,12 +68,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // s_waitcnt immediate: vector-memory count 0 (expcnt, lgkmcnt left alone).
 constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
-template <int NP, int VB>
+template <int NP, int VB, bool PS>
 struct MfmaLayout {
   static constexpr int RS = VB + 4;                 // fp32 row stride of R in LDS
   static constexpr int stage = 2 * NP * kD * 2;     // K, Q bf16 until the Y contraction
-  static constexpr int rbytes = NP * RS * 4;        // R rows, over the dead staging
-  static constexpr int u0 = stage > rbytes ? stage : rbytes;
+  static constexpr int rbytes = NP * RS * 4;        // R rows
+  // R goes over the dead staging, except with one workgroup per state (PS),
+  // which keeps K and Q staged for every column block and gives R its own rows
+  static constexpr int roff = PS ? stage : 0;
+  static constexpr int u0 = PS ? stage + rbytes : (stage > rbytes ? stage : rbytes);
   static constexpr int fb = (int)(sizeof(LevelLds) + sizeof(TreeLds));  // level-scheduled fallback
   static constexpr int bytes = u0 > fb ? u0 : fb;
 };
@@ -222,20 +225,19 @@ __device__ __forceinline__ void split3_bf16(const float (&x)[8], bf16x8& h8, bf1
 template <int NP, int VB>
 constexpr int mfma_waves() { return (NP / 32) * (VB / 32); }
 
-template <int NP, int VB, bool FUSED>
-__global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void verify_mfma_kernel(
+template <int NP, int VB, bool FUSED, bool PS>
+__global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : (PS ? 2 : 3)) void verify_mfma_kernel(
     int H, int N, int mode, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const int32_t* __restrict__ parents,
     const float* S_root, uint16_t* __restrict__ o, float* __restrict__ U,
     int32_t* __restrict__ status, PrevCommit pc) {
-  using Lay = MfmaLayout<NP, VB>;
+  using Lay = MfmaLayout<NP, VB, PS>;
   constexpr int NT = NP / 32;                 // node tiles
   constexpr int CT = VB / 32;                 // value-column tiles in the block
   constexpr int NW = NT * CT;                 // waves
   constexpr int NTH = 64 * NW;                // threads
   static_assert(NW == 4 || NW == 8, "one (node tile, column tile) pair per wave");
-  static_assert(NT != 2 || Lay::bytes >= 4 * 8 * 64 * 16, "room for four waves' partial products");
   constexpr int NVB = kD / VB;
   constexpr int SL = NP > 64 ? 2 : 1;         // tree nodes per lane
   constexpr int NG = NT * (NT + 1);           // lower-triangular blocks of K K^T and K Q^T
@@ -273,19 +275,23 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   const int lm = lane & 31;
   const int hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: wave-uniform branches
-  const int bid = xcd_group(blockIdx.x, gridDim.x, NVB);
-  const int vb = bid % NVB;
-  const int bh = bid / NVB;
+  // One workgroup per (state, column block), or per state (PS), looping over
+  // its NVB column blocks after the tree, the Gram and the path solve, which
+  // then run once per state instead of once per block.
+  const int bid = PS ? (int)blockIdx.x : xcd_group(blockIdx.x, gridDim.x, NVB);
+  const int vb = PS ? 0 : bid % NVB;  // the (first) column block
+  const int bh = PS ? bid : bid / NVB;
   const int h = bh % H;
   const int b = bh / H;
-  const int cbase = vb * VB;
+  int cbase = vb * VB;                // the current column block's first column
   const bool gdn = mode == kGdn;
   // With two node tiles (KS = 2) the two waves of a column tile split the d_k
   // contraction instead of each streaming the whole S block: wave (kh, ct)
   // loads rows 64 kh .. 64 kh + 63 and forms partial products for both node
   // tiles; the halves meet in LDS after the contraction (step 5).  It then
   // owns node tile kh for steps 4, 6 and 7.
-  constexpr int KS = NT == 2 ? 2 : 1;          // d_k split of the S contraction
+  constexpr int KS = (NT == 2 && !PS) ? 2 : 1;  // d_k split of the S contraction
+  static_assert(KS == 1 || Lay::bytes >= 4 * 8 * 64 * 16, "room for four waves' partial products");
   const int nt_w = KS == 2 ? (wave & 1) : wave / CT;    // this wave's node tile
   const int ct_w = KS == 2 ? (wave >> 1) : wave % CT;   // this wave's column tile
   const int akof = 8 * hi;
@@ -506,11 +512,11 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   constexpr int TL = KSTEPS / 2;                // 32-row tiles of those rows
   const int srow0 = KS == 2 ? nt_w * 64 : 0;
   // block base (uniform) + 32-bit lane offset in bytes: scalar-base addressing
-  const size_t sblk = (size_t)bh * kD * kD + cbase + ct_w * 32 + (size_t)srow0 * kD;
+  auto sblk_of = [&](int c) { return (size_t)bh * kD * kD + c + ct_w * 32 + (size_t)srow0 * kD; };
   const uint32_t slane = 4u * (lm + akof * kD);
   float sv[KSTEPS][8];
-  auto load_S = [&]() {
-    const char* Sb = reinterpret_cast<const char*>(S_root + sblk);
+  auto load_S = [&](int c) {
+    const char* Sb = reinterpret_cast<const char*>(S_root + sblk_of(c));
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
@@ -538,18 +544,22 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   // the path solve; the 32-node shape, whose registers are at their limit
   // there, issues them at the update instead.
   constexpr bool kEarlyOps = !(KS == 1 && NT == 1);
-  auto load_prev_ops = [&]() {
+  // k of the path nodes (the same for every column block) and u at column
+  // block c (with_k false: u only)
+  auto load_prev_ops = [&](int c, bool with_k) {
     const int4 e0 = reinterpret_cast<const int4*>(spath.e)[2 * hi];
     const int4 e1 = reinterpret_cast<const int4*>(spath.e)[2 * hi + 1];
     const int ej[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-    const int col = cbase + ct_w * 32 + lm;
+    const int col = c + ct_w * 32 + lm;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       upa[i] = pc.U[((size_t)bh * pc.N + ej[i]) * kD + col];
+      if (with_k) {
 #pragma unroll
-      for (int T = 0; T < TL / 2; ++T)
-        kpd[T][i] = *reinterpret_cast<const uint32_t*>(
-            pc.k + ((size_t)(b * pc.N + ej[i]) * H + h) * kD + srow0 + 64 * T + 2 * lm);
+        for (int T = 0; T < TL / 2; ++T)
+          kpd[T][i] = *reinterpret_cast<const uint32_t*>(
+              pc.k + ((size_t)(b * pc.N + ej[i]) * H + h) * kD + srow0 + 64 * T + 2 * lm);
+      }
     }
   };
   auto prev_apply = [&](const float (&dj)[8]) {
@@ -591,7 +601,7 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
       for (int i = 0; i < 8; ++i) sv[ks][i] *= gam;
     {
       // first 16 path nodes
-      if constexpr (!kEarlyOps) load_prev_ops();
+      if constexpr (!kEarlyOps) load_prev_ops(cbase, true);
       const float4 d0 = reinterpret_cast<const float4*>(spath.pd)[2 * hi];
       const float4 d1 = reinterpret_cast<const float4*>(spath.pd)[2 * hi + 1];
       const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
@@ -629,12 +639,13 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   // barrier after the update), so S_out may be S_in.
   auto store_committed = [&](int ks) {
     if (KS == 1 && NT > 1 && nt_w != 0) return;  // uniform
-    char* So = reinterpret_cast<char*>(pc.S_out + sblk);
+    char* So = reinterpret_cast<char*>(pc.S_out + sblk_of(cbase));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       *reinterpret_cast<float*>(So + slane + 4u * (ks * 16 + i) * kD) = sv[ks][i];
   };
 
+  constexpr int FBW = PS ? kD : VB;  // columns this workgroup covers
   if (Lmax > kMaxL) {
     if constexpr (FUSED) {
       // the previous step's commit of this block, plainly (rare path): the
@@ -668,9 +679,9 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
       const float gam = gsink[1];
       const float* Si = S_root + (size_t)bh * kD * kD;
       float* So = pc.S_out + (size_t)bh * kD * kD;
-      for (int e = tid; e < kD * (VB / 4); e += NTH) {
-        const int r = e / (VB / 4);
-        const int c = cbase + 4 * (e % (VB / 4));
+      for (int e = tid; e < kD * (FBW / 4); e += NTH) {
+        const int r = e / (FBW / 4);
+        const int c = cbase + 4 * (e % (FBW / 4));
         float4 acc = mul4(gam, *reinterpret_cast<const float4*>(Si + r * kD + c));
         for (int t = 0; t < Lp; ++t) {
           const int nd = fpath[t];
@@ -687,7 +698,7 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
     TreeLds& tfb = *reinterpret_cast<TreeLds*>(smem + sizeof(LevelLds));
     build_tree(tfb, parents + (size_t)b * N, N);
     level_solve<uint16_t>(tfb, *reinterpret_cast<LevelLds*>(smem), mode, b, h, H, N, kD, kD, cbase,
-                          cbase + VB, q, k, v, alpha, beta, FUSED ? pc.S_out : S_root, o, U);
+                          cbase + FBW, q, k, v, alpha, beta, FUSED ? pc.S_out : S_root, o, U);
     return;
   }
 
@@ -695,16 +706,17 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   // the matrix-core layout (k of path node 8 hi + i at rows 64 T + 2 lm and
   // + 1 of the wave's S rows, u of that node at the lane's column), issued
   // before the S stream; they are consumed after the path solve.
-  if constexpr (FUSED && kEarlyOps) load_prev_ops();
+  if constexpr (FUSED && kEarlyOps) load_prev_ops(cbase, true);
   // S and V (at the positions the outputs land on) arrive during the Gram and
   // the path solve
-  load_S();
+  load_S(cbase);
   uint2 vv[4];
-  {
-    const uint16_t* vr = v + ((size_t)(b * N + my_n) * H + h) * kD + cbase + col0;
+  auto load_V = [&](int c) {
+    const uint16_t* vr = v + ((size_t)(b * N + my_n) * H + h) * kD + c + col0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) vv[g] = *reinterpret_cast<const uint2*>(vr + 8 * g);
-  }
+  };
+  load_V(cbase);
 
   // ---- 3. ancestor-masked Gram, transposed (lane = node) ----
   {
@@ -830,6 +842,10 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
                     e[12] | (e[13] << 8) | (e[14] << 16) | (e[15] << 24));
   }
 
+  // ---- per column block (one pass, or NVB with one workgroup per state) ----
+#pragma unroll
+  for (int vbi = 0; vbi < (PS ? NVB : 1); ++vbi) {
+  if constexpr (PS) cbase = vbi * VB;
   if constexpr (FUSED) {
     commit_prev();
     // where several waves hold the same block, every wave's S values are in
@@ -877,7 +893,9 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
       qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, qb, qacc, 0, 0, 0);
       qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, qb, qacc, 0, 0, 0);
     }
-    __syncthreads();  // K/Q staging is dead (R takes its place)
+    // K/Q staging is dead (R takes its place); with one workgroup per state, K
+    // and Q stay and every wave is past the previous block's gather of R
+    __syncthreads();
   } else {
     // partial products over this wave's half of d_k, for both node tiles: the
     // own tile (nt_w) accumulates in kacc/qacc, the other in kx/qx
@@ -948,7 +966,7 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
   }
 
   // ---- 6. R = beta (V - gamma KS) into LDS rows ----
-  float* Rsh = reinterpret_cast<float*>(smem);
+  float* Rsh = reinterpret_cast<float*>(smem + Lay::roff);
   const float my_g = sga[my_n];
   if (my_n0 < N) {
     const float bn = sbe[my_n];
@@ -965,6 +983,16 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
         r = vf;
       }
       *reinterpret_cast<float4*>(Rsh + my_n * RS + col0 + 8 * g) = r;
+    }
+  }
+  // one workgroup per state: the next column block's S, V and u are issued
+  // now (their registers are free) and arrive during this block's gather
+  if constexpr (PS) {
+    if (vbi + 1 < NVB) {
+      const int cn = (vbi + 1) * VB;
+      if constexpr (FUSED) load_prev_ops(cn, false);
+      load_S(cn);
+      load_V(cn);
     }
   }
   // this node's path coefficients (both chains) into registers
@@ -1022,27 +1050,21 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : 3) void 
       *reinterpret_cast<uint2*>(orow + 8 * g) = f32x4_to_bf16(o4[g].x, o4[g].y, o4[g].z, o4[g].w);
     }
   }
+  }  // column blocks
 }
 
-template <int NP, int VB>
+template <int NP, int VB, bool FUSED, bool PS>
 static int launch_np_vb(int B, int H, int N, int mode, const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta, const int32_t* parents,
                         const float* S_root, void* o, float* U, int32_t* status, hipStream_t stream,
                         const PrevCommit* prev) {
-  const long long nblocks = (long long)B * H * (kD / VB);
+  const long long nblocks = (long long)B * H * (PS ? 1 : kD / VB);
   if (nblocks > 0x7fffffffLL) return static_cast<int>(hipErrorInvalidConfiguration);
-  if (prev)
-    hipLaunchKernelGGL((verify_mfma_kernel<NP, VB, true>), dim3((unsigned)nblocks),
-                       dim3((64 * mfma_waves<NP, VB>())), 0,
-                       stream, H, N, mode, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta,
-                       parents, S_root, static_cast<uint16_t*>(o), U, status, *prev);
-  else
-    hipLaunchKernelGGL((verify_mfma_kernel<NP, VB, false>), dim3((unsigned)nblocks),
-                       dim3((64 * mfma_waves<NP, VB>())), 0,
-                       stream, H, N, mode, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta,
-                       parents, S_root, static_cast<uint16_t*>(o), U, status, PrevCommit{});
+  hipLaunchKernelGGL((verify_mfma_kernel<NP, VB, FUSED, PS>), dim3((unsigned)nblocks),
+                     dim3((64 * mfma_waves<NP, VB>())), 0, stream, H, N, mode,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), alpha, beta, parents, S_root,
+                     static_cast<uint16_t*>(o), U, status, FUSED ? *prev : PrevCommit{});
   return static_cast<int>(hipGetLastError());
 }
 
@@ -1050,15 +1072,20 @@ int launch_verify_mfma(int B, int H, int N, int mode, const void* q, const void*
                        const float* alpha, const float* beta, const int32_t* parents,
                        const float* S_root, void* o, float* U, int32_t* status,
                        hipStream_t stream, const PrevCommit* prev) {
-  // one wave per (node tile, value-column tile): 4 waves up to 64 nodes, 8 above
+  // Shapes (measured at the 8-, 64- and 128-node workloads):
+  //  - up to 32 nodes: one workgroup per state already (a single 128-column block);
+  //  - up to 64 nodes: verify with one workgroup per state (two per CU, 43-44 us
+  //    against 44.5-45 us); the fused step with one per (state, 64-column block),
+  //    three per CU (57.5-58.5 us against 58-59 us);
+  //  - up to 128 nodes: one workgroup per state (one per CU; 640-650 us against
+  //    885 us for verify, 780-795 us against 1040 us fused).
+#define TV_ARGS B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status, stream, prev
   if (N <= 32)
-    return launch_np_vb<32, 128>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
-                                 stream, prev);
+    return prev ? launch_np_vb<32, 128, true, false>(TV_ARGS) : launch_np_vb<32, 128, false, false>(TV_ARGS);
   if (N <= 64)
-    return launch_np_vb<64, 64>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
-                                stream, prev);
-  return launch_np_vb<128, 64>(B, H, N, mode, q, k, v, alpha, beta, parents, S_root, o, U, status,
-                               stream, prev);
+    return prev ? launch_np_vb<64, 64, true, false>(TV_ARGS) : launch_np_vb<64, 64, false, true>(TV_ARGS);
+  return prev ? launch_np_vb<128, 64, true, true>(TV_ARGS) : launch_np_vb<128, 64, false, true>(TV_ARGS);
+#undef TV_ARGS
 }
 
 }  // namespace tv
