@@ -163,3 +163,40 @@ def test_one_round_pairing_every_output():
     o, st = _run(bt)
     assert not st.any()
     _check(bt, o)
+
+
+@pytest.mark.parametrize("B,Hkv,N,Hq", [
+    (48, 8, 16, 8),    # 384 workgroups, one round: some CUs run one, some a pair
+    (8, 8, 16, 8),     # 64 workgroups, fewer than the CUs
+    (36, 4, 70, 8),    # 288 workgroups of two query blocks each
+    (128, 8, 16, 8),   # 1024 workgroups, several rounds: heaviest first
+    (40, 2, 200, 8),   # 560 workgroups of seven query blocks each
+    (260, 1, 8, 2),    # more sequences than the in-kernel ranking holds: plain order
+])
+def test_work_order_every_output(B, Hkv, N, Hq):
+    """Grids on every branch of the work order (one round with and without
+    pairs, several rounds, unranked): every output checked, with prefix
+    lengths that tie, reach 0 and reach P_max."""
+    rng = np.random.default_rng(B + N)
+    par = np.stack([_rand_tree(rng, N) for _ in range(B)])
+    plen = rng.integers(0, 97, size=B)
+    plen[:6] = [0, 96, 96, 40, 40, 40]
+    bt = synth.make_attention_inputs(seed=B, B=B, N=N, Hq=Hq, Hkv=Hkv, P_max=96, parents=par,
+                                     prefix_len=plen)
+    o, st = _run(bt)
+    assert not st.any()
+    _check(bt, o)
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
+def test_scale_sign_and_zero(scale):
+    """A negative scale (applied with q negated), a zero scale (every visible
+    key weighted alike) and a large one, against the oracle."""
+    rng = np.random.default_rng(41)
+    par = np.stack([_rand_tree(rng, 40) for _ in range(3)])
+    bt = synth.make_attention_inputs(seed=41, B=3, N=40, Hq=8, Hkv=2, P_max=80, parents=par,
+                                     prefix_len=np.array([80, 33, 0]))
+    bt = bt.__class__(**{**bt.__dict__, "scale": scale})
+    o, st = _run(bt)
+    assert not st.any()
+    _check(bt, o)

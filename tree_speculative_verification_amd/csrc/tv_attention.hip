@@ -24,6 +24,8 @@
 //   and V is read in that order from a row-major tile in LDS.
 // A tile's rows are loaded into registers three tiles ahead and written to the
 // other of two LDS buffers while the tile before it is computed.
+#include <atomic>
+
 #include "tv_device.h"
 #include "tv_launch.h"
 
@@ -38,7 +40,7 @@ constexpr int kAKeys = 32;        // keys per tile
 constexpr int kVS = kAD + 8;       // bf16 row stride of the V tile (rows 4 apart on other banks)
 constexpr int kAMaskNodes = kARows + 1;        // nodes a row block can touch
 constexpr int kAWords = kMaxTree / 32;         // ancestor words per node
-constexpr int kBalSeqs = 64;                   // sequences the one-round pairing ranks in LDS
+constexpr int kBalSeqs = kAT;                  // sequences the work order ranks in LDS
 
 typedef __bf16 abf16x8 __attribute__((ext_vector_type(8)));
 typedef short atr4 __attribute__((ext_vector_type(4)));
@@ -66,8 +68,35 @@ __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
   return r;
 }
 
+// Work order.  A workgroup's work follows its sequence's prefix length, so the
+// items (sequence, key/value head, query block) are ranked longest prefix
+// first, and workgroup k takes the item of rank attn_rank(k).  The dispatcher
+// sends workgroup k to XCD k % 8 and fills every CU's first slot before any
+// second one.  When the grid is one round (at most two workgroups per CU) the
+// round lasts as long as its busiest CU: on each XCD the first C workgroups
+// (C = CUs per XCD) take a CU each and the next ones a second slot on the CUs
+// of the first ones, so the heaviest items run alone and the rest pair the
+// heavy with the light.  A longer grid goes heaviest first (each slot that
+// frees takes the next heaviest).  Either way runs of consecutive ranks, the
+// query blocks of one head, which read the same keys and values, stay on one
+// XCD and share its L2.  A bijection on [0, G).
+__device__ __forceinline__ int attn_rank(int k, int G, int ncu, int grp) {
+  constexpr int kX = 8;
+  const int C = ncu / kX;
+  if (C > 0 && G % kX == 0 && G <= 2 * ncu) {
+    const int x = k % kX, j = k / kX, J = G / kX;
+    const int s0 = J < C ? J : C;   // per XCD: workgroups in first slots
+    const int s1 = J - s0;          // and in second slots
+    const int alone = s0 - s1;
+    if (j >= C) return G - 1 - (x * s1 + (j - C));    // light, beside workgroup k - 8 C
+    if (j < s1) return kX * alone + x * s1 + j;        // heavy, paired
+    return x * alone + (j - s1);                       // alone on its CU: the heaviest
+  }
+  return xcd_group(k, G, grp);
+}
+
 __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
-    int N, int Hq, int Hkv, int P_max, int nqb, float scale_log2,
+    int B, int N, int Hq, int Hkv, int P_max, int nqb, int ncu, float scale_log2,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ prefix_len,
     const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
@@ -76,35 +105,29 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lm = lane & 31, hi = lane >> 5;
-  // A workgroup's work follows its sequence's prefix length.  A grid of 512
-  // workgroups is one round at two per CU on the 256 CUs, and the round lasts
-  // as long as its busiest CU.  The dispatcher fills every CU's first slot
-  // before any second one (workgroup k goes to XCD k % 8, its slot-0 and
-  // slot-1 workgroups are k and k + 256), so the items are ranked by prefix
-  // length and the heaviest are paired with the lightest on each CU.
-  // Consecutive ranks stay on one XCD, so the query blocks of a head still
-  // share its key/value tiles through that XCD's L2.  Other grids keep the
-  // plain order.
-  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int bid;
   {
     const int per_b = Hkv * nqb;
-    const int Bn = gridDim.x / per_b;
-    if (gridDim.x == 2 * 256 && Bn <= kBalSeqs) {
+    const int m = attn_rank(blockIdx.x, gridDim.x, ncu, nqb < 16 ? nqb : 16);
+    if (B <= kBalSeqs) {
       __shared__ int sP[kBalSeqs];
       __shared__ int sel;
-      if (tid < Bn) sP[tid] = min(max(prefix_len[tid], 0), P_max);
+      if (tid < B) sP[tid] = min(max(prefix_len[tid], 0), P_max);
       __syncthreads();
-      const int k = blockIdx.x, x = k % 8, j = k / 8;
-      const int m = j < 32 ? x * 32 + j : 511 - (x * 32 + (j - 32));  // rank of the item
-      if (tid < Bn) {  // the sequence of rank m / per_b (longest prefix first, then by index)
+      if (tid < B) {  // the sequence of rank m / per_b (longest prefix first, then by index)
         int c = 0;
-        for (int t = 0; t < Bn; ++t) c += (sP[t] > sP[tid]) || (sP[t] == sP[tid] && t < tid);
+        for (int t = 0; t < B; ++t) c += (sP[t] > sP[tid]) || (sP[t] == sP[tid] && t < tid);
         if (c == m / per_b) sel = tid;
       }
       __syncthreads();
       bid = sel * per_b + m % per_b;
+    } else {
+      bid = m;  // too many sequences to rank here: plain order
     }
   }
+  // everything below that follows from the item is uniform (scalar registers,
+  // scalar branches)
+  bid = __builtin_amdgcn_readfirstlane(bid);
   const int qb = bid % nqb;
   const int bkv = bid / nqb;
   const int kvh = bkv % Hkv;
@@ -121,11 +144,26 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   const int rc = min(row, R - 1);
   const int my_n = rc / G;
   const int hq = kvh * G + rc % G;
+  // A negative scale is applied as its magnitude with q negated (exact in
+  // bf16), so the running maximum can be taken over the unscaled scores.
+  const bool negq = scale_log2 < 0.f;
+  // (a zero scale runs as 1e-30: every visible score then gives exactly 1,
+  // as with 0, and a hidden one, -inf, still gives 0)
+  const float csc = fmaxf(fabsf(scale_log2), 1e-30f);
   abf16x8 qop[8];
   {
     const uint16_t* qr = q + (((size_t)b * N + my_n) * Hq + hq) * kAD + 8 * hi;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) qop[st] = *reinterpret_cast<const abf16x8*>(qr + 16 * st);
+    for (int st = 0; st < 8; ++st) {
+      uint4 w = *reinterpret_cast<const uint4*>(qr + 16 * st);
+      if (negq) {
+        w.x ^= 0x80008000u;
+        w.y ^= 0x80008000u;
+        w.z ^= 0x80008000u;
+        w.w ^= 0x80008000u;
+      }
+      qop[st] = __builtin_bit_cast(abf16x8, w);
+    }
   }
 
   // ---- tree: parents (validated, bad ones treated as -1), ancestor words ----
@@ -156,7 +194,14 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   // (their loads repeat tile T - 1), so the loop body has no branches and the
   // wait counts before each LDS store stay exact
   const int T3 = (T + 2) / 3 * 3;
+  // Uniform row bases of this (sequence, key/value head): its committed cache
+  // rows and its tree rows; a thread adds a 32-bit byte offset (the launch
+  // checks that they fit).
   const size_t cache_bh = ((size_t)b * Hkv + kvh) * P_max;
+  const char* kpre = reinterpret_cast<const char*>(kc + cache_bh * kAD);
+  const char* vpre = reinterpret_cast<const char*>(vc + cache_bh * kAD);
+  const char* ktre = reinterpret_cast<const char*>(kt + ((size_t)b * N * Hkv + kvh) * kAD);
+  const char* vtre = reinterpret_cast<const char*>(vt + ((size_t)b * N * Hkv + kvh) * kAD);
   // Thread's two 16-byte chunks of a tile: chunk c = tid + 256 u, key c / 16,
   // dims 8 (c % 16) .. + 7.  Three register sets: a tile's rows are loaded
   // three iterations before the iteration that computes it, and written to
@@ -164,17 +209,17 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   // source rows of this thread's chunk u (0, 1) of tile t
   auto src_rows = [&](int t, int u, const uint16_t*& kp, const uint16_t*& vp) {
     t = min(t, T - 1);
-    const int c = tid + kAT * u;
-    const int key = c >> 4, ch = c & 15;
-    if (t < TP) {
-      const size_t r = cache_bh + min(t * kAKeys + key, P - 1);
-      kp = kc + r * kAD + 8 * ch;
-      vp = vc + r * kAD + 8 * ch;
+    const int key = (tid >> 4) + 16 * u;
+    const uint32_t chb = 16u * (tid & 15);
+    if (t < TP) {  // uniform
+      const uint32_t off = static_cast<uint32_t>(min(t * kAKeys + key, P - 1)) * (kAD * 2) + chb;
+      kp = reinterpret_cast<const uint16_t*>(kpre + off);
+      vp = reinterpret_cast<const uint16_t*>(vpre + off);
     } else {
-      const int jn = min((t - TP) * kAKeys + key, N - 1);
-      const size_t r = ((size_t)b * N + jn) * Hkv + kvh;
-      kp = kt + r * kAD + 8 * ch;
-      vp = vt + r * kAD + 8 * ch;
+      const uint32_t off =
+          static_cast<uint32_t>(min((t - TP) * kAKeys + key, N - 1) * Hkv) * (kAD * 2) + chb;
+      kp = reinterpret_cast<const uint16_t*>(ktre + off);
+      vp = reinterpret_cast<const uint16_t*>(vtre + off);
     }
   };
   auto store_chunk = [&](int buf, int u, uint4 kv, uint4 vv) {
@@ -221,44 +266,57 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
       const abf16x8 a = *reinterpret_cast<const abf16x8*>(Kr + k_slot(lm, 2 * st + hi) * 8);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], sacc, 0, 0, 0);
     }
-    // visibility: prefix keys below P; tree keys on the query node's root path
-    uint32_t vis = 0u;
-    if (t < TP) {
-      const int left = P - t * kAKeys;
-      vis = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
-    } else if (t < T) {
-      vis = s.anc[(my_n - n_lo) * kAWords + (t - TP)];
-    }
-    float mt = -__builtin_inff();
-    const uint32_t vh = vis >> (4 * hi);  // bit 8 (r/4) + r%4: key 8 (r/4) + 4 hi + r%4
+    // The running maximum m_run (per query, in scaled base-2 units) moves only
+    // when some query of the wave gains more than 2^8 on it (one uniform
+    // branch): until then the probabilities stay below 256, exact to fp32
+    // rounding, and O^T and l need no rescaling.  mt: the tile's largest
+    // visible unscaled score of this lane's query.
+    auto track_max = [&](float mt) {
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float ms = mt * csc;
+      if (__any(ms > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, ms);
+        const float alpha = exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        // O's lane holds queries 8 (r/4) + 4 hi + r%4; their factors sit in
+        // lanes of those queries
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sacc[r] = ((vh >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] * scale_log2 : -__builtin_inff();
-      mt = fmaxf(mt, sacc[r]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // The reference maximum moves only when some query of the wave gains more
-    // than 2^8 on it (one uniform branch): until then the probabilities stay
-    // below 256, exact to fp32 rounding, and O^T and l need no rescaling.
-    if (__any(mt > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-      // O's lane holds queries 8 (r/4) + 4 hi + r%4; their factors sit in
-      // lanes of those queries
+        for (int r = 0; r < 16; ++r) {
+          const float ar = __shfl(alpha, 8 * (r >> 2) + 4 * hi + (r & 3));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float ar = __shfl(alpha, 8 * (r >> 2) + 4 * hi + (r & 3));
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) oacc[dt][r] *= ar;
+          for (int dt = 0; dt < 4; ++dt) oacc[dt][r] *= ar;
+        }
       }
+    };
+    // p = 2^(scale' s - m_run) on the transcendental unit (results below the
+    // fp32 normal range flush to 0: such probabilities vanish against the
+    // maximum's 1 in the sum and in bf16)
+    if ((t + 1) * kAKeys > P) {  // uniform: not a prefix tile whose keys are all visible
+      // visibility: prefix keys below P; tree keys on the query node's root
+      // path; none past the last tile
+      uint32_t vis = 0u;
+      if (t < TP) {
+        vis = (1u << (P - t * kAKeys)) - 1u;  // 1 .. 31 keys left
+      } else if (t < T) {
+        vis = s.anc[(my_n - n_lo) * kAWords + (t - TP)];
+      }
+      const uint32_t vh = vis >> (4 * hi);  // bit 8 (r/4) + r%4: key 8 (r/4) + 4 hi + r%4
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sacc[r] = ((vh >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] : -__builtin_inff();
     }
+    float mt = fmaxf(sacc[0], sacc[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
+    track_max(mt);
+    const float nm = -m_run;
     float psum = 0.f;
     uint32_t pw[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2f(sacc[r] - m_run), p1 = exp2f(sacc[r + 1] - m_run);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], csc, nm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], csc, nm));
       psum += p0 + p1;
       pw[r >> 1] = bf16pair(p0, p1);
     }
@@ -338,6 +396,21 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   }
 }
 
+// Compute units of the current device, asked once per device (0 if the
+// runtime cannot say: the work order then goes heaviest first).
+int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 0;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 }  // namespace
 
 int launch_tree_attention(int B, int N, int Hq, int Hkv, int P_max, float scale, const void* q,
@@ -349,9 +422,13 @@ int launch_tree_attention(int B, int N, int Hq, int Hkv, int P_max, float scale,
   const int nqb = (int)((rows + kARows - 1) / kARows);
   const long long nblocks = (long long)B * Hkv * nqb;
   if (nblocks > 0x7fffffffLL) return static_cast<int>(hipErrorInvalidConfiguration);
+  // 32-bit byte offsets within one (sequence, key/value head): cache rows and tree rows
+  if ((long long)P_max * kAD * 2 > 0xffffffffLL ||
+      (long long)N * Hkv * kAD * 2 > 0xffffffffLL)
+    return static_cast<int>(hipErrorInvalidValue);
   const float scale_log2 = scale * 1.4426950408889634f;  // log2(e): softmax in base 2
-  hipLaunchKernelGGL(tree_attention_kernel, dim3((unsigned)nblocks), dim3(kAT), 0, stream, N, Hq,
-                     Hkv, P_max, nqb, scale_log2, static_cast<const uint16_t*>(q),
+  hipLaunchKernelGGL(tree_attention_kernel, dim3((unsigned)nblocks), dim3(kAT), 0, stream, B, N,
+                     Hq, Hkv, P_max, nqb, device_cus(), scale_log2, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
                      prefix_len, static_cast<const uint16_t*>(k_tree),
                      static_cast<const uint16_t*>(v_tree), parents, static_cast<uint16_t*>(o),
