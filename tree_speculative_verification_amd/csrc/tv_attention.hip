@@ -37,7 +37,10 @@ constexpr int kAT = 256;          // threads per workgroup
 constexpr int kAD = 128;          // head dim
 constexpr int kARows = 128;       // query rows per workgroup
 constexpr int kAKeys = 32;        // keys per tile
-constexpr int kVS = kAD + 8;       // bf16 row stride of the V tile (rows 4 apart on other banks)
+// bf16 row stride of the V tile: 320 B = 80 dwords, so the four rows one
+// transposed read touches per 32 lanes start 16 banks apart and cover all 64
+// banks once (the 272 B stride of a minimal pad overlapped them 4 deep)
+constexpr int kVS = kAD + 32;
 constexpr int kAMaskNodes = kARows + 1;        // nodes a row block can touch
 constexpr int kAWords = kMaxTree / 32;         // ancestor words per node
 constexpr int kBalSeqs = kAT;                  // sequences the work order ranks in LDS
@@ -59,6 +62,12 @@ struct AttnLds {
   uint32_t anc[kAMaskNodes * kAWords];  // inclusive ancestor words of the block's nodes
   int par[kMaxTree];
 };
+
+// max of x over lanes l and l ^ 32 (one lane swap, no LDS round trip)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
   typedef __bf16 v2 __attribute__((ext_vector_type(2)));
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
     // rounding, and O^T and l need no rescaling.  mt: the tile's largest
     // visible unscaled score of this lane's query.
     auto track_max = [&](float mt) {
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = xor32_max(mt);
       const float ms = mt * csc;
       if (__any(ms > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, ms);
