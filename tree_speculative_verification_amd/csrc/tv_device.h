@@ -87,6 +87,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % kXcds) * per + bid / kXcds;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() is a release and
+// acquire fence at workgroup scope over all memory, which makes every wave
+// wait for all its outstanding global loads first, so a load issued for a
+// later phase cannot stay in flight across it.  This one waits for the wave's
+// LDS operations only.  Data moved into LDS by direct-to-LDS loads, and global
+// memory shared between waves, still need their own waits.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Block id -> work item such that each run of g consecutive items (items that
 // share inputs, e.g. the value-column blocks of one state) goes to one XCD and
 // is dispatched together, while the chip as a whole walks the items in order.

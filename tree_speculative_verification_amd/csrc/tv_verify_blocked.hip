@@ -60,11 +60,20 @@ typedef __bf16 bbf16x2 __attribute__((ext_vector_type(2)));
 typedef float bf32x16 __attribute__((ext_vector_type(16)));
 
 template <typename TIn>
-struct BlockedLds {
+struct __align__(16) BlockedLds {  // 16-byte aligned: float4 rows read as one 128-bit access
   static constexpr int kEnt = blocked_entries<TIn>();
-  float U[kMaxTree * kBVB];   // R rows, solved in place into U rows (row stride = columns)
-  TIn QS[kMaxTree * kBVB];    // gamma_n QS_n rows, in the input type
-  float Sst[sizeof(TIn) == 2 ? kBD * kBVB : 1];  // S block of the matrix-core path
+  float U[kMaxTree * kBVB];   // R rows, solved in place into U rows (row stride = columns);
+                              // on the resident matrix-core path first half of the k rows
+  union {
+    TIn QS[kMaxTree * kBVB];  // gamma_n QS_n rows, in the input type
+    struct {                  // resident matrix-core path (gamma QS stays in registers)
+      float kk[kEnt];         // first half of k_n . k_j per entry
+      float Tw[kEnt];         // T = (I + A)^-1 on the entries
+      uint16_t erow[kEnt];    // first entry of the entry's path node (its row)
+    } r;
+  };
+  float Sst[sizeof(TIn) == 2 ? kBD * kBVB : 1];  // S block of the matrix-core path, as
+                                                 // bf16 hi and lo words (stage_s)
   float cA[kEnt];             // decay during the walk, then A = beta_n D (k_n.k_j) (1 on
                               // the node's own entry), then T = (I + A)^-1 if resident
   float cP[kEnt];             // D (q_n.k_j), then the output weights of R if resident
@@ -161,9 +170,7 @@ __device__ __forceinline__ void load_tile_qk(TileIn& t, int node, int N, int H, 
   const uint32_t off = tile_rowoff(node, H) + 16u * hi;
   const size_t base = ((size_t)b * N * H + h) * kBD;
   const char* qr = reinterpret_cast<const char*>(q + base) + off;
-  // branch-free: without the delta rule the k operand is unused and these
-  // loads re-read the q rows just fetched
-  const char* kr = reinterpret_cast<const char*>((gdn ? k : q) + base) + off;
+  const char* kr = reinterpret_cast<const char*>(k + base) + off;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     t.qb[ks] = *reinterpret_cast<const bbf16x8*>(qr + 32 * ks);
@@ -191,47 +198,81 @@ __device__ __forceinline__ float4 load_s_part(const float* __restrict__ blk) {
   return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(blk) + off);
 }
 
-// [K;Q] S_block products of one tile.  A = S block^T (value column x d_k),
-// taken from the S block staged in LDS (row-major, 32 columns) and split into
-// bf16 hi + lo words per 16-row step; B = [K or Q]^T (d_k x node).
-__device__ __forceinline__ void mma_tile(const TileIn& t, const float* Sst, bool gdn,
-                                         bf32x16& kacc, bf32x16& qacc) {
-  const int lane = threadIdx.x & 63;
-  const float* Sl = Sst + 8 * (lane >> 5) * kBVB + (lane & 31);  // rows 16 ks + 8 (lane/32) + i
+// The S block (128 x 32 fp32) is staged once per block for all waves as bf16
+// hi + lo words (x = hi + lo to 16 bits), transposed: value column c holds its
+// 128 rows in 16 chunks of 8 (16 B), chunk j at slot j ^ (c % 16), so the 32
+// columns of one operand read spread over the banks; the hi words fill the
+// first 8192 elements, the lo words the next.
+__device__ __forceinline__ int sst_off(int c, int j) { return c * kBD + ((j ^ (c & 15)) << 3); }
+
+// This thread's float4 of the block (row tid/8, columns 4 (tid%8) + [0, 4)).
+__device__ __forceinline__ void stage_s(float* Sst, float4 x) {
+  uint16_t* sh = reinterpret_cast<uint16_t*>(Sst);
+  const int t = threadIdx.x;
+  const int r = t >> 3, c0 = 4 * (t & 7);
+  const float v[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    kacc[r] = 0.f;
-    qacc[r] = 0.f;
-  }
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    uint32_t wh[4], wl[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x0 = Sl[(16 * ks + 2 * i) * kBVB], x1 = Sl[(16 * ks + 2 * i + 1) * kBVB];
-      wh[i] = pack2_bf16(x0, x1);
-      wl[i] = pack2_bf16(x0 - __uint_as_float(wh[i] << 16), x1 - __uint_as_float(wh[i] & 0xffff0000u));
-    }
-    bbf16x8 shi, slo;
-    __builtin_memcpy(&shi, wh, 16);
-    __builtin_memcpy(&slo, wl, 16);
-    qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, t.qb[ks], qacc, 0, 0, 0);
-    qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, t.qb[ks], qacc, 0, 0, 0);
-    if (gdn) {
-      kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, t.kb[ks], kacc, 0, 0, 0);
-      kacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, t.kb[ks], kacc, 0, 0, 0);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t h = f32_to_bf16(v[i]);
+    const uint16_t l = f32_to_bf16(v[i] - __uint_as_float(static_cast<uint32_t>(h) << 16));
+    const int idx = sst_off(c0 + i, r >> 3) + (r & 7);
+    sh[idx] = h;
+    sh[kBD * kBVB + idx] = l;
   }
 }
 
+// One [K or Q] S_block product of a tile on matrix cores: A = S block^T
+// (value column x d_k) from the staged hi and lo words, B = op^T (d_k x node)
+// from the tile registers.
+__device__ __forceinline__ void mma_pass(const bbf16x8 (&op)[8], const float* Sst, bf32x16& acc) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t* sh = reinterpret_cast<const uint16_t*>(Sst);
+  // opaque, so the operand addresses are formed here at each call rather than
+  // held (spilled) across the column blocks
+  int c = lane & 31;
+  asm volatile("" : "+v"(c));
+  const int hi = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int o = sst_off(c, 2 * ks + hi);
+    const bbf16x8 shi = *reinterpret_cast<const bbf16x8*>(sh + o);
+    const bbf16x8 slo = *reinterpret_cast<const bbf16x8*>(sh + kBD * kBVB + o);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, op[ks], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, op[ks], acc, 0, 0, 0);
+  }
+  // operand reads one step ahead of their products, no further (registers)
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int ks = 0; ks < 7; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+
 // R and gamma QS of one tile into LDS: the accumulator puts node lane%32 and
-// value columns 8 (r/4) + 4 (lane/32) + r%4 in lane `lane`.
-__device__ __forceinline__ void store_tile(BlockedLds<uint16_t>& s, const TileIn& t, int T, int N, bool gdn,
-                                           const bf32x16& kacc, const bf32x16& qacc) {
+// value columns 8 (r/4) + 4 (lane/32) + r%4 in lane `lane`.  Q first, then K,
+// one accumulator at a time.
+__device__ __forceinline__ void contract_store(BlockedLds<uint16_t>& s, const TileIn& t, int T, int N,
+                                               bool gdn) {
   const int lane = threadIdx.x & 63;
   const int n = T * 32 + (lane & 31);
-  if (n >= N) return;
-  const float gn = s.gam[n], bn = s.bet[n];
+  const bool live = n < N;
+  const int nn = live ? n : 0;
+  const float gn = s.gam[nn], bn = s.bet[nn];
+  bf32x16 acc;
+  mma_pass(t.qb, s.Sst, acc);
+  if (live) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      Elem<uint16_t>::store4(s.QS, urow(n, 8 * g + 4 * (lane >> 5), kBVB),
+                             make_float4(gn * acc[4 * g + 0], gn * acc[4 * g + 1],
+                                         gn * acc[4 * g + 2], gn * acc[4 * g + 3]));
+  }
+  if (gdn) mma_pass(t.kb, s.Sst, acc);
+  if (!live) return;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const uint2 w = t.vv[g];
@@ -239,16 +280,12 @@ __device__ __forceinline__ void store_tile(BlockedLds<uint16_t>& s, const TileIn
                                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
     float4 r = vf;
     if (gdn) {
-      r.x = bn * (vf.x - gn * kacc[4 * g + 0]);
-      r.y = bn * (vf.y - gn * kacc[4 * g + 1]);
-      r.z = bn * (vf.z - gn * kacc[4 * g + 2]);
-      r.w = bn * (vf.w - gn * kacc[4 * g + 3]);
+      r.x = bn * (vf.x - gn * acc[4 * g + 0]);
+      r.y = bn * (vf.y - gn * acc[4 * g + 1]);
+      r.z = bn * (vf.z - gn * acc[4 * g + 2]);
+      r.w = bn * (vf.w - gn * acc[4 * g + 3]);
     }
-    const int col = 8 * g + 4 * (lane >> 5);
-    *reinterpret_cast<float4*>(&s.U[urow(n, col, kBVB)]) = r;
-    Elem<uint16_t>::store4(s.QS, urow(n, col, kBVB),
-                           make_float4(gn * qacc[4 * g + 0], gn * qacc[4 * g + 1],
-                                       gn * qacc[4 * g + 2], gn * qacc[4 * g + 3]));
+    *reinterpret_cast<float4*>(&s.U[urow(n, 8 * g + 4 * (lane >> 5), kBVB)]) = r;
   }
 }
 
@@ -259,12 +296,20 @@ __device__ __forceinline__ void store_tile(BlockedLds<uint16_t>& s, const TileIn
 // hold the base row and are not stored).
 __device__ __forceinline__ void contract_keep(BlockedLds<uint16_t>& s, const TileIn& t, int n,
                                               bool gdn, uint2 (&gq)[4]) {
-  bf32x16 kacc, qacc;
-  mma_tile(t, s.Sst, gdn, kacc, qacc);
   const int lane = threadIdx.x & 63;
   const bool live = n >= 0;
   const int nn = live ? n : 0;
   const float gn = s.gam[nn], bn = s.bet[nn];
+  bf32x16 acc;
+  mma_pass(t.qb, s.Sst, acc);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    gq[g].x = static_cast<uint32_t>(f32_to_bf16(gn * acc[4 * g + 0])) |
+              (static_cast<uint32_t>(f32_to_bf16(gn * acc[4 * g + 1])) << 16);
+    gq[g].y = static_cast<uint32_t>(f32_to_bf16(gn * acc[4 * g + 2])) |
+              (static_cast<uint32_t>(f32_to_bf16(gn * acc[4 * g + 3])) << 16);
+  }
+  if (gdn) mma_pass(t.kb, s.Sst, acc);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const uint2 w = t.vv[g];
@@ -272,16 +317,12 @@ __device__ __forceinline__ void contract_keep(BlockedLds<uint16_t>& s, const Til
                                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
     float4 r = vf;
     if (gdn) {
-      r.x = bn * (vf.x - gn * kacc[4 * g + 0]);
-      r.y = bn * (vf.y - gn * kacc[4 * g + 1]);
-      r.z = bn * (vf.z - gn * kacc[4 * g + 2]);
-      r.w = bn * (vf.w - gn * kacc[4 * g + 3]);
+      r.x = bn * (vf.x - gn * acc[4 * g + 0]);
+      r.y = bn * (vf.y - gn * acc[4 * g + 1]);
+      r.z = bn * (vf.z - gn * acc[4 * g + 2]);
+      r.w = bn * (vf.w - gn * acc[4 * g + 3]);
     }
     if (live) *reinterpret_cast<float4*>(&s.U[urow(n, 8 * g + 4 * (lane >> 5), kBVB)]) = r;
-    gq[g].x = static_cast<uint32_t>(f32_to_bf16(gn * qacc[4 * g + 0])) |
-              (static_cast<uint32_t>(f32_to_bf16(gn * qacc[4 * g + 1])) << 16);
-    gq[g].y = static_cast<uint32_t>(f32_to_bf16(gn * qacc[4 * g + 2])) |
-              (static_cast<uint32_t>(f32_to_bf16(gn * qacc[4 * g + 3])) << 16);
   }
 }
 
@@ -308,7 +349,7 @@ __device__ __forceinline__ void gather_owner(BlockedLds<uint16_t>& s, const uint
 #pragma unroll 2
     for (int t = 0; t < L; ++t) {
       const int e = s.en[x + t];
-      const float wt = s.cA[x + t], wp = s.cP[x + t];
+      const float wt = s.r.Tw[x + t], wp = s.cP[x + t];
       const float4 r0 = *reinterpret_cast<const float4*>(&s.U[urow(e, ca, kBVB)]);
       const float4 r1 = *reinterpret_cast<const float4*>(&s.U[urow(e, cc, kBVB)]);
       a0 = fma4(wp, r0, a0);
@@ -477,7 +518,7 @@ __device__ __forceinline__ void level_solve(BlockedLds<TIn>& s, int p0, int p1, 
       }
       *reinterpret_cast<float4*>(&s.U[urow(n, col, vb)]) = u;
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -505,6 +546,131 @@ __device__ __forceinline__ void chunk_outputs(BlockedLds<TIn>& s, int p0, int p1
     *reinterpret_cast<float4*>(U + ((size_t)bh * N + n) * dv + c0 + col) =
         *reinterpret_cast<const float4*>(&s.U[urow(n, col, vb)]);
   }
+}
+
+// ---- resident trees on the matrix-core path: Gram values from the tiles ----
+//
+// The q and k tiles are loaded into registers once, before the Gram: each
+// lane pair (lm, lm + 32) of wave w holds the node at depth-order position
+// 32 w + lm (elements 16 ks + 8 (lane/32) + [0, 8)).  The k rows are staged
+// in LDS one half of d_k at a time (64 bf16 a row, 64 KB for 512 nodes, over
+// the R rows, which are not in use yet), and each lane pair forms its node's
+// path products q_n . k_j and k_n . k_j against the staged rows: every q and
+// k row is read from memory once.
+
+// Path walk that also records, for each entry, the first entry of the
+// entry's node (its row): entry t of node n is (n, e_t) with D(e_t -> n).
+template <typename TIn>
+__device__ __forceinline__ void walk_entries_rows(BlockedLds<TIn>& s, int N) {
+  for (int p = threadIdx.x; p < N; p += kBT) {
+    const int n = s.ord[p];
+    int x = s.off[p];
+    float D = 1.f;
+    for (int e = n; e >= 0; e = s.par[e]) {
+      s.en[x] = static_cast<uint16_t>(e);
+      s.r.erow[x] = static_cast<uint16_t>(s.off[s.jmp[e]]);
+      s.cA[x] = D;
+      D *= s.alp[e];
+      ++x;
+    }
+  }
+}
+
+// Staged half of a k row: 8 chunks of 16 B (chunk c = elements 8 c .. 8 c + 7
+// of the half) at slot c ^ (row % 8), so lanes reading chunk c of different
+// rows spread over the banks.
+__device__ __forceinline__ int kst_off(int row, int c) { return row * 64 + ((c ^ (row & 7)) << 3); }
+
+__device__ __forceinline__ float dot8_bf16x8(bbf16x8 a, uint4 b, float acc) {
+  uint4 ua;
+  __builtin_memcpy(&ua, &a, 16);
+  return dot8_bf16(ua, b, acc);
+}
+
+// Sum over lanes l and l ^ 32.
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Gram values of every entry from the register tiles: cP = D (q_n.k_j),
+// cA = beta_n D (k_n.k_j) (1 on the node's own entry); pos = the lane's
+// depth-order position, n its node (-1: none).
+__device__ __forceinline__ void gram_tiles(BlockedLds<uint16_t>& s, const TileIn& t, int pos, int n) {
+  const int lane = threadIdx.x & 63;
+  const int hi = lane >> 5;
+  uint16_t* Kst = reinterpret_cast<uint16_t*>(s.U);
+  const bool live = n >= 0;
+  const int x0 = live ? s.off[pos] : 0;
+  const int L = live ? s.len[n] : 0;
+  const int Lw = __builtin_amdgcn_readfirstlane(__reduce_max_sync(~0ull, L));  // wave's longest path
+  const float bn = live ? s.bet[n] : 0.f;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (live) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bbf16x8 w = t.kb[4 * half + j];
+        *reinterpret_cast<bbf16x8*>(Kst + kst_off(n, 2 * j + hi)) = w;
+      }
+    }
+    lds_barrier();  // the half's k rows staged
+    for (int i = 0; i < Lw; ++i) {
+      const int e = i < L ? s.en[x0 + i] : (live ? n : 0);
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 ke = *reinterpret_cast<const uint4*>(Kst + kst_off(e, 2 * j + hi));
+        sq = dot8_bf16x8(t.qb[4 * half + j], ke, sq);
+        sk = dot8_bf16x8(t.kb[4 * half + j], ke, sk);
+      }
+      sq = xor32_sum(sq);
+      sk = xor32_sum(sk);
+      if (hi == 0 && i < L) {
+        const int x = x0 + i;
+        if (half == 0) {
+          s.cP[x] = sq;
+          s.r.kk[x] = sk;
+        } else {
+          const float D = s.cA[x];
+          s.cP[x] = D * (s.cP[x] + sq);
+          s.cA[x] = i > 0 ? bn * D * (s.r.kk[x] + sk) : 1.f;  // beta is 0 without the delta rule
+        }
+      }
+    }
+    lds_barrier();  // the half's products are read (and the rows are free)
+  }
+}
+
+// T = (I + A)^-1 and the output weights, node by node (no depth levels).  Row
+// n of T restricted to n's path e_0 = n, e_1, ... solves x (I + A) = e_n:
+//   x_0 = 1,  x_s = - sum_{t<s} x_t A[e_t, e_s],
+// where A[e_t, e_s] is entry s - t of e_t's own row (e_s sits s - t steps above
+// e_t).  The output weights W[n, e_s] = sum_{t<=s} Pc[n, e_t] T[e_t, e_s] need
+// the ancestors' T rows, so they follow a barrier; they replace Pc in place
+// (entry s reads entries t <= s of its own row only, so s runs downwards).
+__device__ __forceinline__ void path_inverse(BlockedLds<uint16_t>& s, int N) {
+  for (int p = threadIdx.x; p < N; p += kBT) {
+    const int x0 = s.off[p];
+    const int L = s.len[s.ord[p]];
+    s.r.Tw[x0] = 1.f;
+    for (int sp = 1; sp < L; ++sp) {
+      float acc = s.cA[x0 + sp];  // t = 0: x_0 A[n, e_s] with x_0 = 1
+      for (int t = 1; t < sp; ++t) acc = fmaf(s.r.Tw[x0 + t], s.cA[s.r.erow[x0 + t] + (sp - t)], acc);
+      s.r.Tw[x0 + sp] = -acc;
+    }
+  }
+  lds_barrier();
+  for (int p = threadIdx.x; p < N; p += kBT) {
+    const int x0 = s.off[p];
+    const int L = s.len[s.ord[p]];
+    for (int sp = L - 1; sp >= 0; --sp) {
+      float acc = s.cP[x0 + sp];  // t = s: T[e_s, e_s] = 1
+      for (int t = 0; t < sp; ++t) acc = fmaf(s.cP[x0 + t], s.r.Tw[s.r.erow[x0 + t] + (sp - t)], acc);
+      s.cP[x0 + sp] = acc;
+    }
+  }
+  lds_barrier();
 }
 
 // ---- resident trees: the solve as a product with the inverse ----
@@ -550,11 +716,11 @@ __device__ __forceinline__ void tree_inverse(BlockedLds<TIn>& s, int N) {
         dst[r] = x + sp;
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int r = 0; r < kItemsPerThread; ++r)
       if (dst[r] >= 0) s.cA[dst[r]] = val[r];
-    __syncthreads();
+    lds_barrier();
   }
   // output weights of every entry (all T rows are final)
   const int nent = s.off[N];
@@ -576,13 +742,13 @@ __device__ __forceinline__ void tree_inverse(BlockedLds<TIn>& s, int N) {
       val[r] = acc;
     }
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int r = 0; r < kItemsPerThread; ++r) {
     const int x = threadIdx.x + r * kBT;
     if (x < nent) s.cP[x] = val[r];
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // u_n and o_n of every node for value columns [c0, c0 + vb) from the R rows
@@ -668,9 +834,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
 #define TV_CONTRACT(c0)                                                                    \
   if constexpr (MFMA) {                                                                    \
     if (wave < ntiles) {                                                                   \
-      bf32x16 kacc, qacc;                                                                  \
-      mma_tile(t0, s.Sst, gdn, kacc, qacc);                                                \
-      store_tile(s, t0, wave, N, gdn, kacc, qacc);                                         \
+      contract_store(s, t0, wave, N, gdn);                                                 \
     }                                                                                      \
   } else {                                                                                 \
     contract_fma<TIn>(s, N, H, dk, dv, vb, b, h, bh, (c0), gdn, q, k, v, S_root);          \
@@ -711,7 +875,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
       s.len[tid] = static_cast<int16_t>(s.len[tid] + nl);
       s.gam[tid] *= ng;
     }
-    __syncthreads();
+    lds_barrier();
   }
   // counting sort by depth
   int my_d = 0;
@@ -720,7 +884,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     atomicAdd(&s.hist[my_d], 1);
     atomicMax(&s.maxd, my_d);
   }
-  __syncthreads();
+  lds_barrier();
   const int maxd = s.maxd;
   for (int d = tid; d <= maxd + 1; d += kBT) {
     int c = 0, e = 0;
@@ -732,7 +896,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     s.lst[d] = c;
     s.ebase[d] = e;
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < N) {
     const int pos = s.lst[my_d] + atomicSub(&s.hist[my_d], 1) - 1;
     s.ord[pos] = static_cast<int16_t>(tid);
@@ -741,8 +905,8 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
   }
   if (tid == 0) s.off[N] = s.ebase[maxd + 1];
   if (h == 0 && tid == 0 && status) status[b] = bad ? 1 : 0;
-  if constexpr (MFMA) reinterpret_cast<float4*>(s.Sst)[tid] = snext;
-  __syncthreads();
+  if constexpr (MFMA) stage_s(s.Sst, snext);
+  lds_barrier();
 
   // Chunks of path entries, as many as LDS holds.  When the whole tree's
   // entries fit (one chunk), they are walked, given their Gram values and
@@ -758,29 +922,27 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
       // and stay in registers for every column block (no re-reads), gamma QS
       // stays in the accumulator lanes, and each lane finishes the outputs of
       // its own node
-      walk_entries(s, 0, N, 0);
-      __syncthreads();
-      gram_entries<TIn, MFMA>(s, 0, N, 0, N, H, dk, b, h, gdn, q, k);
-      __syncthreads();
       // tile T holds the nodes at depth-order positions 32 T .. 32 T + 31:
       // the lanes of a wave finish nodes of one depth, so their loops over
       // the path entries end together
       const int pj = 32 * wave + (tid & 31);
       const int myn = pj < N ? s.ord[pj] : -1;
       TV_LOAD_QK(myn, true)
-      TV_LOAD_V(myn, 0, true)
-      if (gdn) tree_inverse(s, N);
+      walk_entries_rows(s, N);
+      lds_barrier();
+      gram_tiles(s, t0, pj, myn);
+      path_inverse(s, N);
       for (int cb = 0;;) {
         const int c0 = cb * vb;
         uint2 gq[4];
+        TV_LOAD_V(myn, c0, true)  // needed at the end of the contraction
         contract_keep(s, t0, myn, gdn, gq);
         const bool more = cb + 1 < nvb;
         TV_LOAD_S(c0 + vb, more)
-        TV_LOAD_V(myn, c0 + vb, more)
-        __syncthreads();  // R rows in LDS
+        lds_barrier();  // R rows in LDS
         gather_owner(s, gq, myn, N, H, b, h, bh, c0, o, U);
-        if (more) reinterpret_cast<float4*>(s.Sst)[tid] = snext;  // the block's products are done
-        __syncthreads();
+        if (more) stage_s(s.Sst, snext);  // the block's products are done
+        lds_barrier();
         if (!more) break;
         ++cb;
       }
@@ -792,9 +954,9 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     // the first block's node tiles load during the inverse (not before: every
     // workgroup would fetch them at once and the tree build would wait)
     walk_entries(s, 0, N, 0);
-    __syncthreads();
+    lds_barrier();
     gram_entries<TIn, MFMA>(s, 0, N, 0, N, H, dk, b, h, gdn, q, k);
-    __syncthreads();
+    lds_barrier();
     TV_LOAD_QK(idn, true)
     TV_LOAD_V(idn, 0, true)
     if (gdn) tree_inverse(s, N);
@@ -811,14 +973,14 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
       p1 = chunk_end(s, p0, N);  // N at once when resident
       if (!resident) {
         walk_entries(s, p0, p1, e0);
-        __syncthreads();
+        lds_barrier();
         gram_entries<TIn, MFMA>(s, p0, p1, e0, N, H, dk, b, h, gdn, q, k);
       }
-      __syncthreads();
+      lds_barrier();
       if (p1 == N) break;
       if (gdn) level_solve(s, p0, p1, e0, vb);
       chunk_outputs(s, p0, p1, e0, vb, N, H, dv, b, h, bh, c0, o, U);
-      __syncthreads();
+      lds_barrier();
       p0 = p1;
     }
     const bool more = cb + 1 < nvb;
@@ -831,14 +993,14 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
       chunk_outputs(s, p0, N, e0, vb, N, H, dv, b, h, bh, c0, o, U);
     }
     if constexpr (MFMA) {
-      if (more) reinterpret_cast<float4*>(s.Sst)[tid] = snext;  // the block's products are done
+      if (more) stage_s(s.Sst, snext);  // the block's products are done
     }
     TV_LOAD_V(idn, c0 + vb, more)
-    __syncthreads();
+    lds_barrier();
     if (!more) break;
     ++cb;
     TV_CONTRACT(c0 + vb)
-    __syncthreads();
+    lds_barrier();
   }
 #undef TV_LOAD_S
 #undef TV_LOAD_QK
