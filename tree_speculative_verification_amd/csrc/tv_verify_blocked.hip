@@ -92,6 +92,25 @@ struct __align__(16) BlockedLds {  // 16-byte aligned: float4 rows read as one 1
   int maxd;
 };
 
+// OR of x over the workgroup with an LDS-only barrier (no wait for this
+// wave's outstanding global loads), for the tree index only: the votes sit
+// at the start of the R rows, which are not in use before the contraction.
+// Each wave posts its vote to its own slot of round r % 2, so no slot needs
+// clearing; a round's slots are read after its barrier and written again two
+// rounds later, past at least one more barrier.
+template <typename TIn>
+__device__ __forceinline__ bool workgroup_or(BlockedLds<TIn>& s, bool x, int r) {
+  int* vote = reinterpret_cast<int*>(s.U) + (r & 1) * (kBT / 64);
+  const int wave = threadIdx.x >> 6;
+  const int any = __any(x) ? 1 : 0;
+  if ((threadIdx.x & 63) == 0) vote[wave] = any;
+  lds_barrier();
+  int acc = 0;
+#pragma unroll
+  for (int w = 0; w < kBT / 64; ++w) acc |= vote[w];
+  return acc != 0;
+}
+
 __device__ __forceinline__ float dpp_sum8(float x) {
   // sum over the 8 lanes of a group: swap neighbours, swap pairs, then
   // mirror within the 8 (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror)
@@ -855,10 +874,10 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     s.len[tid] = 1;
     s.gam[tid] = a_in;
   }
-  const bool bad = __syncthreads_or(my_bad) != 0;
+  const bool bad = workgroup_or(s, my_bad, 0);
   // pointer jumping: a node's span (path nodes from it up to, not including,
   // its jump target) absorbs the target's span until the jump runs off the root
-  while (true) {
+  for (int round = 1;; ++round) {
     int j = -1, nj = -1, nl = 0;
     float ng = 1.f;
     if (tid < N) {
@@ -869,7 +888,7 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
         ng = s.gam[j];
       }
     }
-    if (!__syncthreads_or(j >= 0)) break;
+    if (!workgroup_or(s, j >= 0, round)) break;
     if (j >= 0) {
       s.jmp[tid] = static_cast<int16_t>(nj);
       s.len[tid] = static_cast<int16_t>(s.len[tid] + nl);
