@@ -227,7 +227,8 @@ __device__ __forceinline__ int sst_off(int c, int j) { return c * kBD + ((j ^ (c
 // This thread's float4 of the block (row tid/8, columns 4 (tid%8) + [0, 4)).
 __device__ __forceinline__ void stage_s(float* Sst, float4 x) {
   uint16_t* sh = reinterpret_cast<uint16_t*>(Sst);
-  const int t = threadIdx.x;
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));  // addresses formed at each call, not held across the blocks
   const int r = t >> 3, c0 = 4 * (t & 7);
   const float v[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -244,13 +245,12 @@ __device__ __forceinline__ void stage_s(float* Sst, float4 x) {
 // (value column x d_k) from the staged hi and lo words, B = op^T (d_k x node)
 // from the tile registers.
 __device__ __forceinline__ void mma_pass(const bbf16x8 (&op)[8], const float* Sst, bf32x16& acc) {
-  const int lane = threadIdx.x & 63;
   const uint16_t* sh = reinterpret_cast<const uint16_t*>(Sst);
   // opaque, so the operand addresses are formed here at each call rather than
   // held (spilled) across the column blocks
-  int c = lane & 31;
-  asm volatile("" : "+v"(c));
-  const int hi = lane >> 5;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int c = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
@@ -276,7 +276,8 @@ __device__ __forceinline__ void mma_pass(const bbf16x8 (&op)[8], const float* Ss
 // one accumulator at a time.
 __device__ __forceinline__ void contract_store(BlockedLds<uint16_t>& s, const TileIn& t, int T, int N,
                                                bool gdn) {
-  const int lane = threadIdx.x & 63;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // row addresses formed here, not held across the blocks
   const int n = T * 32 + (lane & 31);
   const bool live = n < N;
   const int nn = live ? n : 0;
@@ -315,7 +316,8 @@ __device__ __forceinline__ void contract_store(BlockedLds<uint16_t>& s, const Ti
 // hold the base row and are not stored).
 __device__ __forceinline__ void contract_keep(BlockedLds<uint16_t>& s, const TileIn& t, int n,
                                               bool gdn, uint2 (&gq)[4]) {
-  const int lane = threadIdx.x & 63;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(n), "+v"(lane));  // R row addresses formed here, not held across the blocks
   const bool live = n >= 0;
   const int nn = live ? n : 0;
   const float gn = s.gam[nn], bn = s.bet[nn];
@@ -1004,7 +1006,6 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     }
     const bool more = cb + 1 < nvb;
     TV_LOAD_S(c0 + vb, more)
-    TV_LOAD_QK(idn, more)
     if (resident) {
       gather_outputs(s, vb, N, H, dv, b, h, bh, c0, o, U);
     } else {
@@ -1014,10 +1015,13 @@ __global__ __launch_bounds__(kBT) void verify_blocked_kernel(
     if constexpr (MFMA) {
       if (more) stage_s(s.Sst, snext);  // the block's products are done
     }
-    TV_LOAD_V(idn, c0 + vb, more)
     lds_barrier();
     if (!more) break;
     ++cb;
+    // the next block's tiles load only now: holding them through the chunks'
+    // solves would take more registers than a workgroup of 1024 has
+    TV_LOAD_QK(idn, true)
+    TV_LOAD_V(idn, c0 + vb, true)
     TV_CONTRACT(c0 + vb)
     lds_barrier();
   }
