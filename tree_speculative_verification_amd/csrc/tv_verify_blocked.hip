@@ -670,25 +670,70 @@ __device__ __forceinline__ void gram_tiles(BlockedLds<uint16_t>& s, const TileIn
 // e_t).  The output weights W[n, e_s] = sum_{t<=s} Pc[n, e_t] T[e_t, e_s] need
 // the ancestors' T rows, so they follow a barrier; they replace Pc in place
 // (entry s reads entries t <= s of its own row only, so s runs downwards).
+//
+// Paths of up to kPathRegs nodes keep a row in registers and go through it
+// ancestor by ancestor: after x_t is final, its products with e_t's own row
+// (entries 1, 2, ... of that row, at consecutive addresses) are added to the
+// later x_s.  Longer paths run the same sums through LDS.
+constexpr int kPathRegs = 16;
+
 __device__ __forceinline__ void path_inverse(BlockedLds<uint16_t>& s, int N) {
   for (int p = threadIdx.x; p < N; p += kBT) {
     const int x0 = s.off[p];
     const int L = s.len[s.ord[p]];
-    s.r.Tw[x0] = 1.f;
-    for (int sp = 1; sp < L; ++sp) {
-      float acc = s.cA[x0 + sp];  // t = 0: x_0 A[n, e_s] with x_0 = 1
-      for (int t = 1; t < sp; ++t) acc = fmaf(s.r.Tw[x0 + t], s.cA[s.r.erow[x0 + t] + (sp - t)], acc);
-      s.r.Tw[x0 + sp] = -acc;
+    if (L <= kPathRegs) {
+      float acc[kPathRegs];
+#pragma unroll
+      for (int sp = 0; sp < kPathRegs; ++sp) acc[sp] = (sp > 0 && sp < L) ? s.cA[x0 + sp] : 0.f;
+      s.r.Tw[x0] = 1.f;
+#pragma unroll
+      for (int t = 1; t < kPathRegs; ++t) {
+        if (t < L) {
+          const float xt = -acc[t];
+          s.r.Tw[x0 + t] = xt;
+          const float* At = s.cA + s.r.erow[x0 + t];
+#pragma unroll
+          for (int sp = t + 1; sp < kPathRegs; ++sp)
+            if (sp < L) acc[sp] = fmaf(xt, At[sp - t], acc[sp]);
+        }
+      }
+    } else {
+      s.r.Tw[x0] = 1.f;
+      for (int sp = 1; sp < L; ++sp) {
+        float acc = s.cA[x0 + sp];  // t = 0: x_0 A[n, e_s] with x_0 = 1
+        for (int t = 1; t < sp; ++t) acc = fmaf(s.r.Tw[x0 + t], s.cA[s.r.erow[x0 + t] + (sp - t)], acc);
+        s.r.Tw[x0 + sp] = -acc;
+      }
     }
   }
   lds_barrier();
   for (int p = threadIdx.x; p < N; p += kBT) {
     const int x0 = s.off[p];
     const int L = s.len[s.ord[p]];
-    for (int sp = L - 1; sp >= 0; --sp) {
-      float acc = s.cP[x0 + sp];  // t = s: T[e_s, e_s] = 1
-      for (int t = 0; t < sp; ++t) acc = fmaf(s.cP[x0 + t], s.r.Tw[s.r.erow[x0 + t] + (sp - t)], acc);
-      s.cP[x0 + sp] = acc;
+    if (L <= kPathRegs) {
+      float w[kPathRegs];
+#pragma unroll
+      for (int sp = 0; sp < kPathRegs; ++sp) w[sp] = 0.f;
+#pragma unroll
+      for (int t = 0; t < kPathRegs; ++t) {
+        if (t < L) {
+          const float pt = s.cP[x0 + t];
+          const float* Tt = s.r.Tw + s.r.erow[x0 + t];
+          w[t] += pt;  // T[e_t, e_t] = 1
+#pragma unroll
+          for (int sp = t + 1; sp < kPathRegs; ++sp)
+            if (sp < L) w[sp] = fmaf(pt, Tt[sp - t], w[sp]);
+        }
+      }
+#pragma unroll
+      for (int sp = 0; sp < kPathRegs; ++sp)
+        if (sp < L) s.cP[x0 + sp] = w[sp];
+    } else {
+      for (int sp = L - 1; sp >= 0; --sp) {
+        float acc = s.cP[x0 + sp];  // t = s: T[e_s, e_s] = 1
+        for (int t = 0; t < sp; ++t) acc = fmaf(s.cP[x0 + t], s.r.Tw[s.r.erow[x0 + t] + (sp - t)], acc);
+        s.cP[x0 + sp] = acc;
+      }
     }
   }
   lds_barrier();
