@@ -22,7 +22,7 @@
 //   O += P V with P rounded to bf16: the score accumulator is already P's
 //   operand layout when the k-steps take keys in the accumulator's row order,
 //   and V is read in that order from a row-major tile in LDS.
-// A tile's rows are loaded into registers three tiles ahead and written to the
+// A tile's rows are loaded into registers four tiles ahead and written to the
 // other of two LDS buffers while the tile before it is computed.
 #include <atomic>
 
@@ -199,10 +199,10 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   // ---- key tiles: prefix tiles [0, TP), then tree tiles up to node n_hi ----
   const int TP = (P + kAKeys - 1) / kAKeys;
   const int T = TP + n_hi / kAKeys + 1;
-  // the loop runs in steps of three tiles; tiles past T are fully masked
+  // the loop runs in steps of four tiles; tiles past T are fully masked
   // (their loads repeat tile T - 1), so the loop body has no branches and the
   // wait counts before each LDS store stay exact
-  const int T3 = (T + 2) / 3 * 3;
+  const int T4 = (T + 3) / 4 * 4;
   // Uniform row bases of this (sequence, key/value head): its committed cache
   // rows and its tree rows; a thread adds a 32-bit byte offset (the launch
   // checks that they fit).
@@ -212,8 +212,8 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   const char* ktre = reinterpret_cast<const char*>(kt + ((size_t)b * N * Hkv + kvh) * kAD);
   const char* vtre = reinterpret_cast<const char*>(vt + ((size_t)b * N * Hkv + kvh) * kAD);
   // Thread's two 16-byte chunks of a tile: chunk c = tid + 256 u, key c / 16,
-  // dims 8 (c % 16) .. + 7.  Three register sets: a tile's rows are loaded
-  // three iterations before the iteration that computes it, and written to
+  // dims 8 (c % 16) .. + 7.  Four register sets: a tile's rows are loaded
+  // four iterations before the iteration that computes it, and written to
   // LDS one iteration before.
   // source rows of this thread's chunk u (0, 1) of tile t
   auto src_rows = [&](int t, int u, const uint16_t*& kp, const uint16_t*& vp) {
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
     *reinterpret_cast<uint4*>(&s.K[buf][key * kAD + k_slot(key, ch) * 8]) = kv;
     *reinterpret_cast<uint4*>(&s.V[buf][key * kVS + 8 * ch]) = vv;
   };
-  // three register sets (X = A, B, C) of two chunks of K and V each
-  uint4 kA0, kA1, vA0, vA1, kB0, kB1, vB0, vB1, kC0, kC1, vC0, vC1;
+  // four register sets (X = A, B, C, D) of two chunks of K and V each
+  uint4 kA0, kA1, vA0, vA1, kB0, kB1, vB0, vB1, kC0, kC1, vC0, vC1, kD0, kD1, vD0, vD1;
 #define TV_LOAD(X, t)                                              \
   {                                                                \
     const uint16_t *kp_, *vp_;                                     \
@@ -320,6 +320,8 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
     for (int r = 2; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
     track_max(mt);
     const float nm = -m_run;
+    // l sums the probabilities as rounded to bf16 for the value product (one
+    // two-way dot product with (1, 1) per pair)
     float psum = 0.f;
     uint32_t pw[8];
 #pragma unroll
@@ -362,25 +364,27 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   // q (and the tree's loads) have landed before the pipeline starts, so no
   // wait inside the loop is held up by them
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-  // pipeline: tile t + 3 loaded, tile t computed, tile t + 1 stored, barrier;
-  // set X holds tile t + 1 (to store) and set Y receives tile t + 3 (its
+  // pipeline: tile t + 4 loaded, tile t computed, tile t + 1 stored, barrier;
+  // set X holds tile t + 1 (to store) and set Y receives tile t + 4 (its
   // previous tile t is in LDS already)
   TV_LOAD(A, 0)
   TV_LOAD(B, 1)
   TV_LOAD(C, 2)
+  TV_LOAD(D, 3)
   TV_STORE(A, 0)
   __syncthreads();  // first tile and the ancestor words visible
 #define TV_ATTN_STEP(t, X, Y) \
   do {                        \
-    TV_LOAD(Y, (t) + 3)       \
+    TV_LOAD(Y, (t) + 4)       \
     compute_tile(t);          \
     TV_STORE(X, (t) + 1)      \
     __syncthreads();          \
   } while (0)
-  for (int t = 0; t < T3; t += 3) {
+  for (int t = 0; t < T4; t += 4) {
     TV_ATTN_STEP(t, B, A);
     TV_ATTN_STEP(t + 1, C, B);
-    TV_ATTN_STEP(t + 2, A, C);
+    TV_ATTN_STEP(t + 2, D, C);
+    TV_ATTN_STEP(t + 3, A, D);
   }
 #undef TV_ATTN_STEP
 #undef TV_LOAD
