@@ -207,14 +207,18 @@ __device__ __forceinline__ void load_tile_v(TileIn& t, int node, int N, int H, i
   for (int g = 0; g < 4; ++g) t.vv[g] = *reinterpret_cast<const uint2*>(vr + 16 * g);
 }
 
-// This thread's float4 of a 128 x 32 S block (row tid/8, columns 4 (tid%8) +
-// [0, 4)); the lane offset is opaque so that no 64-bit address is held
-// across the phases between two blocks.
+// This thread's 2 x 2 part of a 128 x 32 S block: rows r0, r0 + 1 with r0 =
+// 2 (tid/16), columns c0, c0 + 1 with c0 = 2 (tid%16), as (S[r0][c0],
+// S[r0][c0+1], S[r0+1][c0], S[r0+1][c0+1]); the lane offset is opaque so
+// that no 64-bit address is held across the phases between two blocks.
 __device__ __forceinline__ float4 load_s_part(const float* __restrict__ blk) {
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));
-  const uint32_t off = static_cast<uint32_t>(((t >> 3) * kBD + 4 * (t & 7)) * 4);
-  return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(blk) + off);
+  const uint32_t off = static_cast<uint32_t>((2 * (t >> 4) * kBD + 2 * (t & 15)) * 4);
+  const char* p = reinterpret_cast<const char*>(blk) + off;
+  const float2 a = *reinterpret_cast<const float2*>(p);
+  const float2 c = *reinterpret_cast<const float2*>(p + kBD * 4);
+  return make_float4(a.x, a.y, c.x, c.y);
 }
 
 // The S block (128 x 32 fp32) is staged once per block for all waves as bf16
@@ -224,20 +228,22 @@ __device__ __forceinline__ float4 load_s_part(const float* __restrict__ blk) {
 // first 8192 elements, the lo words the next.
 __device__ __forceinline__ int sst_off(int c, int j) { return c * kBD + ((j ^ (c & 15)) << 3); }
 
-// This thread's float4 of the block (row tid/8, columns 4 (tid%8) + [0, 4)).
+// This thread's 2 x 2 part of the block (load_s_part): per column, the two
+// rows' hi words go out as one 32-bit store, and the lo words as another.
 __device__ __forceinline__ void stage_s(float* Sst, float4 x) {
   uint16_t* sh = reinterpret_cast<uint16_t*>(Sst);
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));  // addresses formed at each call, not held across the blocks
-  const int r = t >> 3, c0 = 4 * (t & 7);
-  const float v[4] = {x.x, x.y, x.z, x.w};
+  const int r0 = 2 * (t >> 4), c0 = 2 * (t & 15);
+  const float v0[2] = {x.x, x.y}, v1[2] = {x.z, x.w};  // rows r0 and r0 + 1
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint16_t h = f32_to_bf16(v[i]);
-    const uint16_t l = f32_to_bf16(v[i] - __uint_as_float(static_cast<uint32_t>(h) << 16));
-    const int idx = sst_off(c0 + i, r >> 3) + (r & 7);
-    sh[idx] = h;
-    sh[kBD * kBVB + idx] = l;
+  for (int i = 0; i < 2; ++i) {
+    const uint16_t h0 = f32_to_bf16(v0[i]), h1 = f32_to_bf16(v1[i]);
+    const uint16_t l0 = f32_to_bf16(v0[i] - __uint_as_float(static_cast<uint32_t>(h0) << 16));
+    const uint16_t l1 = f32_to_bf16(v1[i] - __uint_as_float(static_cast<uint32_t>(h1) << 16));
+    const int idx = sst_off(c0 + i, r0 >> 3) + (r0 & 7);  // even: a whole 32-bit word
+    *reinterpret_cast<uint32_t*>(sh + idx) = h0 | (static_cast<uint32_t>(h1) << 16);
+    *reinterpret_cast<uint32_t*>(sh + kBD * kBVB + idx) = l0 | (static_cast<uint32_t>(l1) << 16);
   }
 }
 
