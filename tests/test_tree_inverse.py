@@ -3,7 +3,10 @@ on the CPU: for a tree, T = (I + A)^-1 with A[n, j] = beta_n D(j->n) (k_n.k_j)
 on strict ancestors j of n (TreeWY abstract's system) is nonzero only where j
 is on n's root path, and its rows follow
     T[n, e_s] = - sum_{t=1..s} A[n, e_t] T[e_t, e_s]
-over n's path e_0 = n, e_1 = parent(n), ...  Then U = T R and
+over n's path e_0 = n, e_1 = parent(n), ...; equally, row n alone solves
+x (I + A) = e_n on the path: x_0 = 1, x_s = - sum_{t<s} x_t A[e_t, e_s], where
+A[e_t, e_s] is entry s - t of e_t's own row (the node-by-node form the
+resident matrix-core path uses).  Then U = T R and
 o_n = gamma_n QS_n + sum_s W[n, e_s] R_{e_s} with
     W[n, e_s] = sum_{t<=s} D(e_t->n) (q_n.k_{e_t}) T[e_t, e_s]."""
 import numpy as np
@@ -55,6 +58,13 @@ def test_inverse_is_path_supported_and_follows_the_recurrence(seed, N, forest):
         for s in range(1, len(p)):
             rec = -sum(A[n, p[t]] * T[p[t], p[s]] for t in range(1, s + 1))
             assert abs(T[n, p[s]] - rec) < 1e-12
+    for n in range(N):                                 # row n alone, node by node
+        p = _path(par, n)
+        x = [1.0]
+        for s in range(1, len(p)):
+            # A[e_t, e_s] read as entry s - t of e_t's own path row
+            x.append(-sum(x[t] * A[p[t], _path(par, p[t])[s - t]] for t in range(s)))
+        assert np.allclose(x, [T[n, e] for e in p], atol=1e-12)
     # outputs through T match a direct solve
     R = rng.standard_normal((N, 4))
     U = np.linalg.solve(np.eye(N) + A, R)
