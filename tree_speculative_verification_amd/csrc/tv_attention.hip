@@ -269,12 +269,21 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
     af32x16 sacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    // the eight K operand reads go out four ahead of the dependent matrix
+    // instructions (one read in flight left each product waiting on LDS)
     const uint16_t* Kr = s.K[buf] + lm * kAD;
+    abf16x8 ka[8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const abf16x8 a = *reinterpret_cast<const abf16x8*>(Kr + k_slot(lm, 2 * st + hi) * 8);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], sacc, 0, 0, 0);
+    for (int st = 0; st < 8; ++st) ka[st] = *reinterpret_cast<const abf16x8*>(Kr + k_slot(lm, 2 * st + hi) * 8);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qop[st], sacc, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // The running maximum m_run (per query, in scaled base-2 units) moves only
     // when some query of the wave gains more than 2^8 on it (one uniform
     // branch): until then the probabilities stay below 256, exact to fp32
