@@ -379,7 +379,7 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
-    ap.add_argument("--cpu-reps", type=int, default=3,
+    ap.add_argument("--cpu-reps", type=int, default=5,
                     help="passes of the CPU oracle over the sampled sequences")
     ap.add_argument("--no-snapshot-baseline", action="store_true",
                     help="skip timing the per-node-snapshot baseline kernels")
