@@ -515,13 +515,15 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : (PS ? 2 
   auto sblk_of = [&](int c) { return (size_t)bh * kD * kD + c + ct_w * 32 + (size_t)srow0 * kD; };
   const uint32_t slane = 4u * (lm + akof * kD);
   float sv[KSTEPS][8];
-  auto load_S = [&](int c) {
+  auto load_S_ks = [&](int c, int ks) {
     const char* Sb = reinterpret_cast<const char*>(S_root + sblk_of(c));
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
+    for (int i = 0; i < 8; ++i)
+      sv[ks][i] = *reinterpret_cast<const float*>(Sb + slane + 4u * (ks * 16 + i) * kD);
+  };
+  auto load_S = [&](int c) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        sv[ks][i] = *reinterpret_cast<const float*>(Sb + slane + 4u * (ks * 16 + i) * kD);
+    for (int ks = 0; ks < KSTEPS; ++ks) load_S_ks(c, ks);
   };
 
   // ---- fused commit of the previous step (TreeWY abstract: only the accepted
@@ -885,6 +887,11 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : (PS ? 2 
       if constexpr (FUSED) store_committed(ks);
       bf16x8 shi, slo;
       split(ks, shi, slo);
+      // one workgroup per state: the next column block's S rows of this step
+      // go out as soon as this step's registers are split
+      if constexpr (PS) {
+        if (vbi + 1 < NVB) load_S_ks((vbi + 1) * VB, ks);
+      }
       const int so = kq_slot(lm, 2 * ks + hi) * 8;
       const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kn + so);
       const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qn + so);
@@ -991,7 +998,7 @@ __global__ __launch_bounds__((64 * mfma_waves<NP, VB>()), NP > 64 ? 1 : (PS ? 2 
     if (vbi + 1 < NVB) {
       const int cn = (vbi + 1) * VB;
       if constexpr (FUSED) load_prev_ops(cn, false);
-      load_S(cn);
+      if constexpr (KS != 1) load_S(cn);  // (with KS = 1 they went out during the contraction)
       load_V(cn);
     }
   }
