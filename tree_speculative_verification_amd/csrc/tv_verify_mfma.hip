@@ -117,10 +117,11 @@ __device__ __forceinline__ T node_val(const T (&x)[SL], int j) {
   return v;
 }
 
-// Pointer jumping: each round a node adopts the span of the node its jump
-// pointer names (ancestor set, product of alpha) and jumps past it, so spans
-// double until every jump pointer runs off the root.  Spans stay contiguous
-// path segments whether or not the named node already moved this round.
+// Pointer jumping: at each jump step a node adopts the span of the node its
+// jump pointer names (ancestor set, product of alpha) and jumps past it, so
+// spans double until every jump pointer runs off the root.  Spans stay
+// contiguous path segments whether or not the named node already moved in the
+// same step.
 // Returns the tree's longest path length (same in every wave) and flags
 // parents outside [-1, i-1] (treated as -1).
 template <int SL>
