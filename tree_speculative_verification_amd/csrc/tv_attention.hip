@@ -37,10 +37,7 @@ constexpr int kAT = 256;          // threads per workgroup
 constexpr int kAD = 128;          // head dim
 constexpr int kARows = 128;       // query rows per workgroup
 constexpr int kAKeys = 32;        // keys per tile
-// bf16 row stride of the V tile: 320 B = 80 dwords, so the four rows one
-// transposed read touches per 32 lanes start 16 banks apart and cover all 64
-// banks once (the 272 B stride of a minimal pad overlapped them 4 deep)
-constexpr int kVS = kAD + 32;
+constexpr int kABuf = 4;          // LDS tile buffers (a barrier every second tile)
 constexpr int kAMaskNodes = kARows + 1;        // nodes a row block can touch
 constexpr int kAWords = kMaxTree / 32;         // ancestor words per node
 constexpr int kBalSeqs = kAT;                  // sequences the work order ranks in LDS
@@ -56,9 +53,15 @@ typedef float af32x16 __attribute__((ext_vector_type(16)));
 // over all banks.
 __device__ __forceinline__ int k_slot(int row, int ch) { return ch ^ (row & 15); }
 
+// V tile rows are 256 B too; chunk c of row r sits at slot c ^ (4 (r & 3)).  A
+// transposed read covers, per 32 lanes, four consecutive rows and one 64-byte
+// group of four chunks in each; the swizzle puts the four rows' groups on
+// four different 16-bank quarters, so the read touches every bank once.
+__device__ __forceinline__ int v_slot(int row, int ch) { return ch ^ (4 * (row & 3)); }
+
 struct AttnLds {
-  uint16_t K[2][kAKeys * kAD];        // key tile, swizzled chunks
-  uint16_t V[2][kAKeys * kVS];        // value tile, row-major, padded rows
+  uint16_t K[kABuf][kAKeys * kAD];    // key tiles, swizzled chunks
+  uint16_t V[kABuf][kAKeys * kAD];    // value tiles, swizzled chunks
   uint32_t anc[kAMaskNodes * kAWords];  // inclusive ancestor words of the block's nodes
   int par[kMaxTree];
 };
@@ -66,7 +69,7 @@ struct AttnLds {
 // max of x over lanes l and l ^ 32 (one lane swap, no LDS round trip)
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
@@ -213,14 +216,24 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   const char* vtre = reinterpret_cast<const char*>(vt + ((size_t)b * N * Hkv + kvh) * kAD);
   // Thread's two 16-byte chunks of a tile: chunk c = tid + 256 u, key c / 16,
   // dims 8 (c % 16) .. + 7.  Four register sets: a tile's rows are loaded
-  // four iterations before the iteration that computes it, and written to
-  // LDS one iteration before.
+  // five iterations before the iteration that computes it, and written to
+  // LDS two iterations before.
   // source rows of this thread's chunk u (0, 1) of tile t
   auto src_rows = [&](int t, int u, const uint16_t*& kp, const uint16_t*& vp) {
     t = min(t, T - 1);
     const int key = (tid >> 4) + 16 * u;
     const uint32_t chb = 16u * (tid & 15);
-    if (t < TP) {  // uniform
+    if (t + 1 < TP) {  // uniform: all 32 rows are committed rows (t * 32 + key < P)
+      const char* kb = kpre + static_cast<size_t>(t * kAKeys + 16 * u) * (kAD * 2);
+      const char* vb = vpre + static_cast<size_t>(t * kAKeys + 16 * u) * (kAD * 2);
+      uint32_t lo = 16u * tid;
+      // (opaque per use: the compiler otherwise hoists 64-bit lane pointers
+      // into registers; this way the load takes a scalar base and a 32-bit
+      // lane offset)
+      asm volatile("" : "+v"(lo));
+      kp = reinterpret_cast<const uint16_t*>(kb + lo);
+      vp = reinterpret_cast<const uint16_t*>(vb + lo);
+    } else if (t < TP) {  // uniform
       const uint32_t off = static_cast<uint32_t>(min(t * kAKeys + key, P - 1)) * (kAD * 2) + chb;
       kp = reinterpret_cast<const uint16_t*>(kpre + off);
       vp = reinterpret_cast<const uint16_t*>(vpre + off);
@@ -235,7 +248,7 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
     const int c = tid + kAT * u;
     const int key = c >> 4, ch = c & 15;
     *reinterpret_cast<uint4*>(&s.K[buf][key * kAD + k_slot(key, ch) * 8]) = kv;
-    *reinterpret_cast<uint4*>(&s.V[buf][key * kVS + 8 * ch]) = vv;
+    *reinterpret_cast<uint4*>(&s.V[buf][key * kAD + v_slot(key, ch) * 8]) = vv;
   };
   // four register sets (X = A, B, C, D) of two chunks of K and V each
   uint4 kA0, kA1, vA0, vA1, kB0, kB1, vB0, vB1, kC0, kC1, vC0, vC1, kD0, kD1, vD0, vD1;
@@ -251,8 +264,8 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   }
 #define TV_STORE(X, t)                                             \
   {                                                                \
-    store_chunk((t) & 1, 0, k##X##0, v##X##0);                     \
-    store_chunk((t) & 1, 1, k##X##1, v##X##1);                     \
+    store_chunk((t) & 3, 0, k##X##0, v##X##0);                     \
+    store_chunk((t) & 3, 1, k##X##1, v##X##1);                     \
   }
 
   af32x16 oacc[4];
@@ -262,9 +275,9 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
 
-  // one key tile from LDS buffer t & 1 into the running softmax and O^T
+  // one key tile from LDS buffer t % 4 into the running softmax and O^T
   auto compute_tile = [&](int t) {
-    const int buf = t & 1;
+    const int buf = t & 3;
     // S^T = K Q^T: this lane holds keys 8 (r/4) + 4 hi + r%4 of the tile for query lm
     af32x16 sacc;
 #pragma unroll
@@ -324,13 +337,15 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
       for (int r = 0; r < 16; ++r)
         sacc[r] = ((vh >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] : -__builtin_inff();
     }
-    float mt = fmaxf(sacc[0], sacc[1]);
+    // (the NaN-propagating maximum takes three scores per instruction with no
+    // canonicalising moves)
+    float mt = __builtin_elementwise_maximum(sacc[0], sacc[1]);
 #pragma unroll
-    for (int r = 2; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
+    for (int r = 2; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, sacc[r]);
     track_max(mt);
     const float nm = -m_run;
-    // l sums the probabilities as rounded to bf16 for the value product (one
-    // two-way dot product with (1, 1) per pair)
+    // l sums the probabilities in fp32 (the value product takes them rounded
+    // to bf16)
     float psum = 0.f;
     uint32_t pw[8];
 #pragma unroll
@@ -351,18 +366,21 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
     // of group g addresses columns 16 (g % 2) + 4 q .. + 3 of key row
     // 4 (g / 2) + j (+ 16 h2, + 8 for the second half of the k-step), and lane
     // (column n, hi) gets keys 4 hi + (0..3) of its column.
-    const uint16_t* vtr = s.V[buf] + (4 * (lane >> 5) + ((lane >> 2) & 3)) * kVS +
-                          16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // (with the swizzle, row 4 (lane / 32) + j, j = lane / 4 % 4, holds column
+    // group dt at group dt ^ j)
+    const int vj = (lane >> 2) & 3;
+    const uint16_t* vtr = s.V[buf] + (4 * (lane >> 5) + vj) * kAD + 4 * (lane & 1) +
+                          8 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1));
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       abf16x8 pa;
       __builtin_memcpy(&pa, &pw[4 * h2], 16);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* v0 = vtr + 16 * h2 * kVS + 32 * dt;
+        const uint16_t* v0 = vtr + 16 * h2 * kAD + 32 * (dt ^ vj);
         // (C casts: the generic pointer into the LDS tile to an LDS pointer)
         const atr4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4*)(v0));
-        const atr4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4*)(v0 + 8 * kVS));
+        const atr4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4*)(v0 + 8 * kAD));
         const atr8 w = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         const abf16x8 vb = __builtin_bit_cast(abf16x8, w);
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, oacc[dt], 0, 0, 0);
@@ -373,29 +391,34 @@ __global__ __launch_bounds__(kAT, 2) void tree_attention_kernel(
   // q (and the tree's loads) have landed before the pipeline starts, so no
   // wait inside the loop is held up by them
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-  // pipeline: tile t + 4 loaded, tile t computed, tile t + 1 stored, barrier;
-  // set X holds tile t + 1 (to store) and set Y receives tile t + 4 (its
-  // previous tile t is in LDS already)
+  // pipeline: tile t + 5 loaded, tile t computed from LDS buffer t % 4, tile
+  // t + 2 stored, and a barrier after every second tile.  Register set
+  // t % 4 holds tile t from its load until its store; buffer (t + 2) % 4 held
+  // tile t - 2, whose readers have passed a barrier since.
   TV_LOAD(A, 0)
   TV_LOAD(B, 1)
   TV_LOAD(C, 2)
   TV_LOAD(D, 3)
   TV_STORE(A, 0)
-  __syncthreads();  // first tile and the ancestor words visible
-#define TV_ATTN_STEP(t, X, Y) \
-  do {                        \
-    TV_LOAD(Y, (t) + 4)       \
-    compute_tile(t);          \
-    TV_STORE(X, (t) + 1)      \
-    __syncthreads();          \
-  } while (0)
+  TV_STORE(B, 1)
+  TV_LOAD(A, 4)
+  __syncthreads();  // first two tiles and the ancestor words visible
   for (int t = 0; t < T4; t += 4) {
-    TV_ATTN_STEP(t, B, A);
-    TV_ATTN_STEP(t + 1, C, B);
-    TV_ATTN_STEP(t + 2, D, C);
-    TV_ATTN_STEP(t + 3, A, D);
+    TV_LOAD(B, t + 5)
+    compute_tile(t);
+    TV_STORE(C, t + 2)
+    TV_LOAD(C, t + 6)
+    compute_tile(t + 1);
+    TV_STORE(D, t + 3)
+    __syncthreads();
+    TV_LOAD(D, t + 7)
+    compute_tile(t + 2);
+    TV_STORE(A, t + 4)
+    TV_LOAD(A, t + 8)
+    compute_tile(t + 3);
+    TV_STORE(B, t + 5)
+    __syncthreads();
   }
-#undef TV_ATTN_STEP
 #undef TV_LOAD
 #undef TV_STORE
 
