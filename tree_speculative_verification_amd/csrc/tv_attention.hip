@@ -22,8 +22,8 @@
 //   O += P V with P rounded to bf16: the score accumulator is already P's
 //   operand layout when the k-steps take keys in the accumulator's row order,
 //   and V is read in that order from a row-major tile in LDS.
-// A tile's rows are loaded into registers four tiles ahead and written to the
-// other of two LDS buffers while the tile before it is computed.
+// A tile's rows are loaded into registers five tiles ahead and written to one
+// of four LDS buffers two tiles ahead; one barrier covers two tiles.
 #include <atomic>
 
 #include "tv_device.h"
