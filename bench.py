@@ -96,11 +96,36 @@ def algorithmic_bytes(bt):
     return int(verify), int(commit), int(fused), L
 
 
+def code_text(src):
+    """C++ source without comments and with whitespace runs collapsed, so that
+    comment-only edits keep a counter record valid and any code change does not."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":  # string or character literal, copied as is
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def sources_sha(kind, large=False):
     h = hashlib.sha256()
     for rel in (KERNEL_SOURCES_LARGE if large else KERNEL_SOURCES)[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -64,3 +64,13 @@ def test_counter_traffic_needs_matching_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("verify", 4) is None  # no record
     # trees above 128 nodes are hashed over the blocked kernel's sources
     assert bench.sources_sha("verify", large=True) != bench.sources_sha("verify")
+
+
+def test_code_text_ignores_comments_only():
+    base = 'int f(int a) {\n  // note\n  return a + 1; /* why */\n}\nconst char* s = "x // y";\n'
+    reworded = 'int f(int a) {\n  // a different note\n  return a + 1;   /* another */\n}\nconst char* s = "x // y";\n'
+    assert bench.code_text(base) == bench.code_text(reworded)
+    assert bench.code_text(base) != bench.code_text(base.replace("a + 1", "a + 2"))
+    # text inside string literals is code, comment markers included
+    assert bench.code_text(base) != bench.code_text(base.replace('"x // y"', '"x // z"'))
+    assert '"x // y"' in bench.code_text(base)
