@@ -15,12 +15,6 @@
 #include "tv_device.h"
 #include "tv_launch.h"
 
-// Below this many (sequence, head) states, d_v = 128 commits split each state
-// over two workgroups.
-#ifndef TV_COMMIT_SPLIT_BELOW
-#define TV_COMMIT_SPLIT_BELOW 512
-#endif
-
 namespace tv {
 
 __global__ __launch_bounds__(kThreads) void index_kernel(int N, const int32_t* __restrict__ parents,
@@ -266,15 +260,17 @@ static int commit_launch(int B, int H, int N, int dk, const void* k, const float
   return static_cast<int>(hipGetLastError());
 }
 
-// Tiles of 128 rows (the whole state at d_k = 128); at d_v = 128 with few
-// states, 64-row tiles give twice the workgroups to spread over the CUs.
+// Tiles of 128 rows (the whole state at d_k = 128); at d_v = 128, 32-row
+// tiles: four workgroups per state, so the grid drains in small pieces (at
+// 8192 states a launch took 194 us against 213 with whole-state tiles, and
+// 1024 states are as fast either way).
 template <typename TK, int DV>
 static int commit_dv(int B, int H, int N, int dk, const void* k, const float* alpha, const float* U,
                      const int32_t* parents, const int32_t* accepted, const float* S_root,
                      float* S_out, int32_t* path_out, int32_t* status, hipStream_t stream) {
   if constexpr (DV == 128) {
-    if ((long long)B * H < TV_COMMIT_SPLIT_BELOW && dk > 64)
-      return commit_launch<TK, DV, DV / 16>(B, H, N, dk, k, alpha, U, parents, accepted, S_root,
+    if (dk > 64)
+      return commit_launch<TK, DV, DV / 32>(B, H, N, dk, k, alpha, U, parents, accepted, S_root,
                                             S_out, path_out, status, stream);
   }
   return commit_launch<TK, DV, DV / 8>(B, H, N, dk, k, alpha, U, parents, accepted, S_root, S_out,
