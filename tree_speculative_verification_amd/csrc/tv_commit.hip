@@ -107,7 +107,9 @@ __global__ __launch_bounds__(kThreads, NMAX > kMaxNodes ? 4 : 1) void commit_ker
   __shared__ __align__(16) float ksh[CH][RT];
 
   const int tid = threadIdx.x;
-  const int bid = blockIdx.x;  // dispatch order: the workgroups share no large inputs
+  // the row tiles of one state go to one XCD together (they share the path's
+  // U rows through its L2), while the chip walks the states in order
+  const int bid = xcd_group(blockIdx.x, gridDim.x, ntiles);
   const int tile = bid % ntiles;
   const int bh = bid / ntiles;
   const int h = bh % H;
