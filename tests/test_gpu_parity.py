@@ -276,12 +276,16 @@ def test_node_tile_shapes_agree_with_level_solver(N):
     _check(bt, b, ref)
 
 
-def test_commit_alone_with_oracle_pseudo_values():
-    """Feed the oracle's U (rounded to fp32) to the commit kernel: isolates tree_commit."""
+@pytest.mark.parametrize("cfg,B,H", [(4, 6, 5), (4, 3, 1), (4, 32, 8), (2, 4, 8), (3, 8, 32)])
+def test_commit_alone_with_oracle_pseudo_values(cfg, B, H):
+    """Feed the oracle's U (rounded to fp32) to the commit kernel: isolates
+    tree_commit.  The shapes cover state counts whose row tiles fill whole
+    runs of eight XCD groups, a ragged tail of them, and fewer tiles than
+    one run, at d = 128 (32-row tiles) and d = 64."""
     import torch
 
     from tree_speculative_verification_amd import binding as tvb
-    bt = cfg_batch(4).select(np.arange(6), np.arange(5))
+    bt = cfg_batch(cfg).select(np.arange(B), np.arange(H))
     o_ref, U_ref, _ = oracle.verify(bt.mode, bt.parents, bt.q, bt.k, bt.v, bt.alpha, bt.beta, bt.S_root)
     S_ref, _ = oracle.commit(bt.mode, bt.parents, bt.accepted, bt.k, bt.v, bt.alpha, bt.beta, bt.S_root)
     t = synth.to_torch(bt)
