@@ -76,14 +76,15 @@ __global__ __launch_bounds__(kMaxTree) void index_wide_kernel(int N,
 }
 
 // One workgroup per (sequence, head, tile of RT = RPP * P state rows); with
-// P = DV / 8 a tile is 128 rows, i.e. the whole d_k x d_v state at d_k = 128.
-// Thread t owns float4 column group t % CG of rows r0 + t / CG + p * RPP.
+// P = DV / 8 a tile is 128 rows, i.e. the whole d_k x d_v state at d_k = 128
+// (the launcher takes smaller tiles at d_v = 128).  Thread t owns float4
+// column group t % CG of rows r0 + t / CG + p * RPP.
 //
-// Timeline of a workgroup: every state load is issued at once (after the few
-// small loads the path walk needs), the path is walked from the accepted node
-// while they are in flight, then the path's U rows and k entries are staged
-// in LDS (one dependent round trip), and the rank-len(a) update is applied in
-// registers and stored.
+// Timeline of a workgroup: every state load of the tile is issued at once
+// (after the few small loads the path walk needs); the first barrier lets them
+// land; the path is walked from the accepted node; the path's U rows and k
+// entries are staged in LDS (one dependent round trip), and the rank-len(a)
+// update is applied in registers and stored.
 template <typename TK, int DV, int P, int NMAX>
 __global__ __launch_bounds__(kThreads, NMAX > kMaxNodes ? 4 : 1) void commit_kernel(
     int H, int N, int dk, int ntiles, const TK* __restrict__ k, const float* __restrict__ alpha,
