@@ -79,15 +79,27 @@ def test_tree_shapes(kind):
     _check(bt, o)
 
 
-@pytest.mark.parametrize("N", [1, 31, 129, 300])
+@pytest.mark.parametrize("N", [1, 31, 129, 300, 512])
 def test_sizes_and_ragged_row_blocks(N):
     """Node counts that leave ragged 32-row tiles and 128-row blocks; trees past
-    128 nodes (ancestor words beyond the fourth)."""
+    128 nodes (ancestor words beyond the fourth), up to the largest tree."""
     rng = np.random.default_rng(N)
     par = np.stack([_rand_tree(rng, N, depth=40, fan=3) for _ in range(2)])
     bt = synth.make_attention_inputs(seed=N, B=2, N=N, Hq=12, Hkv=4, P_max=64, parents=par,
                                      prefix_len=np.array([64, 33]))
     o, _ = _run(bt)
+    _check(bt, o)
+
+
+def test_largest_chain():
+    """A 512-node chain: the last node sees all 16 tree tiles and its query
+    block spans the last ancestor words."""
+    N = 512
+    par = np.tile(np.arange(-1, N - 1, dtype=np.int32), (2, 1))
+    bt = synth.make_attention_inputs(seed=5, B=2, N=N, Hq=8, Hkv=4, P_max=96, parents=par,
+                                     prefix_len=np.array([96, 0]))
+    o, st = _run(bt)
+    assert not st.any()
     _check(bt, o)
 
 
